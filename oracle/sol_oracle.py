@@ -1,0 +1,300 @@
+"""CPU oracle for Sol-style routed block-sparse attention (NumPy, float64).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: it is used by the tests, by the package's smoke check
+and by the benchmark's CPU-baseline leg.  It shares no code with the HIP
+library; the only common module is the seeded input generator, which holds
+none of this arithmetic.
+
+What is computed, step by step, and where the pages state it:
+
+1. Pool.  The sequence is cut into 64-row blocks; Q, K and V are mean-pooled
+   per block (Star7 README "MiniMax H3 Activation Chunk & Attention
+   Acceleration", section 工作原理 > Sol: Q64/K64 blocks; comfyui-wiki
+   "Spark-H3" news, Spark-Reweight bullet: mean-pooled K/V summaries).
+2. Score.  Every query block is scored against every key block with the
+   pooled product Qbar_a . Kbar_c (keys-SM121 MiniMax-H3 README, optimisation
+   table, Sol-Attn row: each query block goes to its highest-scoring KV blocks).
+3. Route.  Either a threshold "tau standard deviations above the mean of the
+   block scores" (thakicloud "MiniMax-H3 ComfyUI accel stack", section
+   이 기술은 무엇인가; Star7 README, Sol: tau = 1.0), or a top-K ratio
+   (Spark-H3 news, 워크플로 section: topk_mode = topk_ratio, 0.1 / 0.2).
+   The packed conditioning prefix is kept as an exact KV sink (thakicloud
+   post, same section; Star7 README, Sol: audio-range KV sink) and prefix
+   query rows get full attention (Star7 README, Sol; aikraft.ru news,
+   section "Нововведения версии 2.0": exact_kv_and_rows).
+4. Combine.  Selected blocks are attended exactly; every unselected block is
+   not dropped but contributes once through its K/V centroid, and both kinds
+   of term share one softmax (Star7 README, Sol).  Each centroid logit gets a
+   log-mass bias so that the centroid stands for the block's mass (Spark-H3
+   news, Spark-Reweight bullet and its figure caption: mean pooling gives
+   exp(E[x]) where the block's mass is E[exp(x)]).
+
+Readings where the pages leave a step open (each is argued in the design
+notes of this repository):
+
+* score scale: the routing score is the unscaled Qbar . Kbar; mean/std
+  thresholds and top-K are invariant under a positive scale;
+* std is the population standard deviation over all key blocks of the row,
+  computed two-pass; every key block (prefix and ragged tail included)
+  enters the mean and std;
+* tau = -inf selects every block; tau = +inf selects none (before the sink);
+  otherwise block c is selected iff S_ac >= mean + tau * std;
+* top-K keeps k = clamp(ceil(r * n_b - 1e-6), 1, n_b) blocks (r is the float32
+  ratio; the 1e-6 keeps ratios such as 0.1 * 640 from rounding up), ties
+  going to the lower block index;
+* the prefix sink (every key block holding a row < prefix_len) is OR-ed in
+  after ranking; every query block holding a prefix row is computed densely;
+* the centroid logit uses the individual query row: q_i . Kbar_c * scale;
+* the log-mass bias is log(n_c), n_c = valid rows of block c (64, or the
+  tail count), i.e. the centroid counts as n_c copies of itself;
+* softmax scale 1/sqrt(D) unless given; non-causal; rows past N do not exist
+  (the tail block has n_c < 64 rows);
+* a query row left with no term at all (centroids off and nothing selected)
+  outputs 0.
+
+The one-shot softmax below is the definition; an online softmax differs from
+it only by rounding.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional, Tuple
+
+import numpy as np
+
+BLOCK = 64
+
+__all__ = [
+    "BLOCK",
+    "num_blocks",
+    "block_sizes",
+    "prefix_blocks",
+    "topk_count",
+    "pool",
+    "block_scores",
+    "route",
+    "selection_lists",
+    "attend_block",
+    "forward",
+    "forward_blocks",
+]
+
+
+def num_blocks(N: int) -> int:
+    """n_b = ceil(N / 64)."""
+    return -(-int(N) // BLOCK)
+
+
+def block_sizes(N: int) -> np.ndarray:
+    """Valid row count n_c of every block: 64, except a ragged last block."""
+    nb = num_blocks(N)
+    n = np.full(nb, BLOCK, dtype=np.int64)
+    n[-1] = N - BLOCK * (nb - 1)
+    return n
+
+
+def prefix_blocks(prefix_len: int) -> int:
+    """Blocks that hold at least one packed-prefix row: ceil(prefix_len / 64)."""
+    return -(-int(prefix_len) // BLOCK)
+
+
+def topk_count(topk_ratio: float, nb: int) -> int:
+    """Blocks kept per query block in top-K mode (float32 ratio, see header)."""
+    r = float(np.float32(topk_ratio))
+    return int(min(nb, max(1, math.ceil(r * nb - 1e-6))))
+
+
+def pool(x) -> np.ndarray:
+    """Per-block means of the valid rows.
+
+    x: [B, N, H, D] array of bf16-exact values (float32 or float64).
+    Returns float64 [B, H, n_b, D].
+    """
+    B, N, H, D = x.shape
+    nb = num_blocks(N)
+    out = np.empty((B, H, nb, D), dtype=np.float64)
+    for c in range(nb):
+        rows = np.asarray(x[:, c * BLOCK : min(N, (c + 1) * BLOCK)], dtype=np.float64)
+        out[:, :, c, :] = rows.sum(axis=1) / rows.shape[1]
+    return out
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    """S[b, h, a, c] = Qbar_a . Kbar_c (unscaled)."""
+    return np.matmul(qbar, np.swapaxes(kbar, -1, -2))
+
+
+def route(
+    S: np.ndarray,
+    *,
+    tau: Optional[float] = 1.0,
+    topk_ratio: Optional[float] = None,
+    prefix_len: int = 0,
+) -> Dict[str, np.ndarray]:
+    """Block selection from the score matrix S [B, H, n_b, n_b].
+
+    Returns a dict with ``sel`` (bool [B, H, n_b, n_b]) and, per row, ``mu``,
+    ``sigma`` and ``thr`` (the tau threshold, or the k-th largest score in
+    top-K mode; NaN where the row is dense).
+    """
+    B, H, nb, nb2 = S.shape
+    assert nb == nb2
+    pb = min(nb, prefix_blocks(prefix_len))
+    mu = S.mean(axis=-1)
+    sigma = np.sqrt(((S - mu[..., None]) ** 2).mean(axis=-1))
+    thr = np.full(mu.shape, np.nan)
+    if topk_ratio is not None:
+        k = topk_count(topk_ratio, nb)
+        # Descending score, ties broken towards the lower block index.
+        order = np.argsort(-S, axis=-1, kind="stable")
+        sel = np.zeros(S.shape, dtype=bool)
+        np.put_along_axis(sel, order[..., :k], True, axis=-1)
+        thr = np.take_along_axis(S, order[..., k - 1 : k], axis=-1)[..., 0]
+    else:
+        t = float(np.float32(tau))
+        if t == -math.inf:
+            sel = np.ones(S.shape, dtype=bool)
+        elif t == math.inf:
+            sel = np.zeros(S.shape, dtype=bool)
+            thr = np.full(mu.shape, math.inf)
+        else:
+            thr = mu + t * sigma
+            sel = S >= thr[..., None]
+    # Exact KV sink: every key block that holds a prefix row.
+    sel[..., :pb] = True
+    # Prefix query rows see every key exactly.
+    sel[:, :, :pb, :] = True
+    if pb:
+        thr[:, :, :pb] = np.nan
+    return dict(sel=sel, mu=mu, sigma=sigma, thr=thr)
+
+
+def selection_lists(sel: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Ascending index lists [B, H, n_b, n_b] (padded with -1) and counts."""
+    counts = sel.sum(axis=-1).astype(np.int32)
+    lists = np.full(sel.shape, -1, dtype=np.int32)
+    B, H, nb, _ = sel.shape
+    for b in range(B):
+        for h in range(H):
+            for a in range(nb):
+                idx = np.nonzero(sel[b, h, a])[0]
+                lists[b, h, a, : len(idx)] = idx
+    return lists, counts
+
+
+def attend_block(
+    q_rows: np.ndarray,
+    k_head: np.ndarray,
+    v_head: np.ndarray,
+    kbar_head: np.ndarray,
+    vbar_head: np.ndarray,
+    sel_row: np.ndarray,
+    sizes: np.ndarray,
+    *,
+    scale: float,
+    centroid: bool,
+    logmass: bool,
+) -> np.ndarray:
+    """Output rows of one query block of one head.
+
+    q_rows [n_a, D]; k_head, v_head [N, D]; kbar_head, vbar_head [n_b, D];
+    sel_row bool [n_b].  Exact logits for every valid key of a selected block,
+    one centroid logit per unselected block, one softmax over all of them.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    chosen = np.nonzero(sel_row)[0]
+    keys = np.concatenate(
+        [np.arange(c * BLOCK, c * BLOCK + sizes[c]) for c in chosen]
+    ) if len(chosen) else np.zeros(0, dtype=np.int64)
+    kx = np.asarray(k_head[keys], dtype=np.float64)
+    vx = np.asarray(v_head[keys], dtype=np.float64)
+    logits = [q_rows @ kx.T * scale]
+    values = [vx]
+    if centroid:
+        missed = np.nonzero(~sel_row)[0]
+        y = q_rows @ kbar_head[missed].T * scale
+        if logmass:
+            y = y + np.log(sizes[missed].astype(np.float64))[None, :]
+        logits.append(y)
+        values.append(vbar_head[missed])
+    L = np.concatenate(logits, axis=1)
+    Vall = np.concatenate(values, axis=0)
+    if L.shape[1] == 0:
+        return np.zeros((q_rows.shape[0], q_rows.shape[1]))
+    M = L.max(axis=1, keepdims=True)
+    W = np.exp(L - M)
+    return (W @ Vall) / W.sum(axis=1, keepdims=True)
+
+
+def _prepare(q, k, v, tau, topk_ratio, prefix_len, mask):
+    B, N, H, D = q.shape
+    qbar, kbar, vbar = pool(q), pool(k), pool(v)
+    info = dict(qbar=qbar, kbar=kbar, vbar=vbar)
+    if mask is None:
+        S = block_scores(qbar, kbar)
+        r = route(S, tau=tau, topk_ratio=topk_ratio, prefix_len=prefix_len)
+        info.update(S=S, **r)
+    else:
+        info["sel"] = np.asarray(mask, dtype=bool)
+    return info
+
+
+def forward_blocks(
+    q,
+    k,
+    v,
+    blocks: Iterable[Tuple[int, int, int]],
+    *,
+    tau: Optional[float] = 1.0,
+    topk_ratio: Optional[float] = None,
+    prefix_len: int = 0,
+    centroid: bool = True,
+    logmass: bool = True,
+    sm_scale: Optional[float] = None,
+    mask: Optional[np.ndarray] = None,
+    info: Optional[dict] = None,
+):
+    """Output of selected (b, h, query block) triples, one by one.
+
+    q, k, v: [B, N, H, D] bf16-exact values.  ``mask`` (bool [B,H,n_b,n_b])
+    replaces the routing step when given.  ``info`` lets a caller reuse the
+    pooled tensors and routing of an earlier call on the same inputs.
+    Returns ({(b, h, a): float64 [n_a, D]}, info).
+    """
+    B, N, H, D = q.shape
+    scale = (1.0 / math.sqrt(D)) if not sm_scale else float(sm_scale)
+    if info is None:
+        info = _prepare(q, k, v, tau, topk_ratio, prefix_len, mask)
+    sel = info["sel"]
+    sizes = block_sizes(N)
+    out = {}
+    for b, h, a in blocks:
+        rows = slice(a * BLOCK, a * BLOCK + sizes[a])
+        out[(b, h, a)] = attend_block(
+            q[b, rows, h, :],
+            k[b, :, h, :],
+            v[b, :, h, :],
+            info["kbar"][b, h],
+            info["vbar"][b, h],
+            sel[b, h, a],
+            sizes,
+            scale=scale,
+            centroid=centroid,
+            logmass=logmass,
+        )
+    return out, info
+
+
+def forward(q, k, v, **kw):
+    """Full output [B, N, H, D] float64 plus the routing info."""
+    B, N, H, D = q.shape
+    nb = num_blocks(N)
+    blocks = [(b, h, a) for b in range(B) for h in range(H) for a in range(nb)]
+    parts, info = forward_blocks(q, k, v, blocks, **kw)
+    out = np.empty((B, N, H, D), dtype=np.float64)
+    for (b, h, a), o in parts.items():
+        out[b, a * BLOCK : a * BLOCK + o.shape[0], h, :] = o
+    return out, info
+

@@ -1,0 +1,382 @@
+"""Pins for the CPU oracle, checked against things other than the oracle.
+
+* the dense limit (tau = -inf) against a brute-force softmax and against
+  torch's scaled_dot_product_attention in float64;
+* key blocks with constant rows, where the centroid term is exact, so any
+  routing must reproduce dense attention (pins the per-row centroid logit,
+  the log-mass bias log(n_c) and the ragged tail);
+* an independent full-matrix brute force at N <= 256 that routes from
+  token-level scores and applies one masked softmax over N + n_b columns;
+* hand-derived routing results (tests/golden/route_hand.json) and a
+  closed-form centroid case;
+* invariants: tau monotonicity, top-K counts, convex hull of V, the Jensen
+  bound on centroid mass, prefix rows equal dense rows, and block-permutation
+  equivariance.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import sol_oracle as O
+from block_sparse_video_fp32_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f64(bits):
+    return inputs.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _rand(B, N, H, D, seed):
+    q, k, v = inputs.iid(B, N, H, D, seed)
+    return _f64(q), _f64(k), _f64(v)
+
+
+def dense_reference(q, k, v, scale=None):
+    """softmax(q k^T * scale) v per (b, h), written out directly."""
+    B, N, H, D = q.shape
+    s = (1.0 / math.sqrt(D)) if scale is None else scale
+    out = np.empty_like(q)
+    for b in range(B):
+        for h in range(H):
+            L = q[b, :, h] @ k[b, :, h].T * s
+            W = np.exp(L - L.max(axis=1, keepdims=True))
+            out[b, :, h] = (W / W.sum(axis=1, keepdims=True)) @ v[b, :, h]
+    return out
+
+
+def brute_force(q, k, v, *, tau=1.0, topk_ratio=None, prefix_len=0, centroid=True, logmass=True):
+    """Independent small-N implementation: token-level scores, one masked
+    softmax over [N exact keys | n_b centroids] per query row."""
+    B, N, H, D = q.shape
+    nb = (N + 63) // 64
+    blk = np.arange(N) // 64
+    sizes = np.bincount(blk, minlength=nb).astype(np.float64)
+    ind = np.zeros((N, nb))
+    ind[np.arange(N), blk] = 1.0  # token -> block indicator
+    pb = (prefix_len + 63) // 64
+    scale = 1.0 / math.sqrt(D)
+    out = np.empty_like(q)
+    sels = np.zeros((B, H, nb, nb), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            Q, K, V = q[b, :, h], k[b, :, h], v[b, :, h]
+            T = Q @ K.T  # token scores
+            # block score = mean over the block pair of token scores
+            S = (ind.T @ T @ ind) / np.outer(sizes, sizes)
+            sel = np.zeros((nb, nb), dtype=bool)
+            for a in range(nb):
+                row = S[a]
+                if topk_ratio is not None:
+                    kk = O.topk_count(topk_ratio, nb)
+                    order = np.lexsort((np.arange(nb), -row))
+                    sel[a, order[:kk]] = True
+                elif tau == -math.inf:
+                    sel[a] = True
+                elif tau == math.inf:
+                    pass
+                else:
+                    sel[a] = row >= row.mean() + tau * np.std(row)
+            sel[:, :pb] = True
+            sel[:pb, :] = True
+            sels[b, h] = sel
+            tok = sel[blk][:, blk]  # [N, N] token-level mask
+            Kc = (ind.T @ K) / sizes[:, None]
+            Vc = (ind.T @ V) / sizes[:, None]
+            Lx = np.where(tok, T * scale, -np.inf)
+            Ly = Q @ Kc.T * scale + (np.log(sizes)[None, :] if logmass else 0.0)
+            Ly = np.where(sel[blk] | (not centroid), -np.inf, Ly)
+            L = np.concatenate([Lx, Ly], axis=1)
+            empty = np.isneginf(L).all(axis=1)  # no term at all: output 0
+            L[empty] = 0.0
+            W = np.exp(L - L.max(axis=1, keepdims=True))
+            W[empty] = 0.0
+            den = np.where(empty, 1.0, W.sum(axis=1))
+            out[b, :, h] = (W @ np.concatenate([V, Vc])) / den[:, None]
+    return out, sels
+
+
+# ---------------------------------------------------------------- dense limit
+
+
+@pytest.mark.parametrize("B,N,H,D", [(1, 200, 2, 64), (2, 256, 3, 128), (1, 130, 1, 64)])
+def test_dense_limit_matches_softmax_and_sdpa(B, N, H, D):
+    q, k, v = _rand(B, N, H, D, seed=11 + N)
+    out, info = O.forward(q, k, v, tau=-math.inf)
+    assert info["sel"].all()
+    ref = dense_reference(q, k, v)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    import torch
+
+    t = lambda x: torch.from_numpy(x).permute(0, 2, 1, 3)  # BTHD -> BHTD
+    sdpa = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))
+    np.testing.assert_allclose(out, sdpa.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+
+
+def test_dense_limit_custom_scale():
+    q, k, v = _rand(1, 192, 2, 64, seed=5)
+    out, _ = O.forward(q, k, v, tau=-math.inf, sm_scale=0.37)
+    np.testing.assert_allclose(out, dense_reference(q, k, v, scale=0.37), atol=1e-12)
+
+
+# ------------------------------------------------- centroid exact on constant K
+
+
+def _constant_key_blocks(q, k, seed):
+    rng = np.random.default_rng(seed)
+    B, N, H, D = k.shape
+    k = k.copy()
+    for c in range(0, N, 64):
+        k[:, c : c + 64] = rng.standard_normal((B, 1, H, D))
+    return k
+
+
+@pytest.mark.parametrize(
+    "route",
+    [
+        dict(tau=1.0),
+        dict(tau=0.0),
+        dict(tau=2.5),
+        dict(tau=math.inf),
+        dict(topk_ratio=0.25),
+        dict(tau=1.0, prefix_len=70),
+        dict(topk_ratio=0.1, prefix_len=64),
+    ],
+)
+@pytest.mark.parametrize("N", [256, 200, 333])
+def test_constant_key_blocks_reproduce_dense(route, N):
+    q, k, v = _rand(1, N, 2, 64, seed=3 + N)
+    k = _constant_key_blocks(q, k, seed=N)
+    out, info = O.forward(q, k, v, **route)
+    if route.get("tau") != math.inf:
+        assert not info["sel"].all(), "routing left nothing to approximate"
+    np.testing.assert_allclose(out, dense_reference(q, k, v), rtol=0, atol=1e-12)
+
+
+def test_constant_key_blocks_need_the_log_mass_bias():
+    q, k, v = _rand(1, 200, 2, 64, seed=9)
+    k = _constant_key_blocks(q, k, seed=1)
+    out, _ = O.forward(q, k, v, tau=1.0, logmass=False)
+    assert np.abs(out - dense_reference(q, k, v)).max() > 1e-3
+
+
+# ----------------------------------------------------------- brute force N<=256
+
+
+@pytest.mark.parametrize(
+    "N,H,D,kw",
+    [
+        (256, 2, 64, dict(tau=1.0)),
+        (256, 2, 64, dict(tau=0.3)),
+        (200, 2, 64, dict(tau=1.0)),
+        (255, 1, 128, dict(topk_ratio=0.5)),
+        (256, 2, 64, dict(topk_ratio=0.25, prefix_len=64)),
+        (250, 2, 64, dict(tau=0.5, prefix_len=100)),
+        (256, 2, 64, dict(tau=1.0, centroid=False)),
+        (256, 2, 64, dict(tau=1.0, logmass=False)),
+        (64, 1, 64, dict(tau=1.0)),
+        (1, 1, 64, dict(tau=1.0)),
+        (100, 3, 64, dict(tau=math.inf, prefix_len=10)),
+    ],
+)
+def test_brute_force_small(N, H, D, kw):
+    q, k, v = _rand(2, N, H, D, seed=N * 7 + H)
+    # clustered-ish content so that routing is not trivial
+    q = q + 1.5 * np.sin(np.arange(N) / 20.0)[None, :, None, None]
+    k = q.copy() * 0.5 + k * 0.5
+    out, info = O.forward(q, k, v, **kw)
+    ref, sel = brute_force(q, k, v, **kw)
+    np.testing.assert_array_equal(info["sel"], sel)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_brute_force_clustered_generator():
+    q, k, v = inputs.clustered(1, 256, 2, 64, seed=4)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    out, info = O.forward(q, k, v, tau=1.0)
+    ref, sel = brute_force(q, k, v, tau=1.0)
+    np.testing.assert_array_equal(info["sel"], sel)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------- hand-derived routes
+
+
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "route_hand.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_route_hand_examples(case):
+    if "S" in case:
+        S = np.array(case["S"], dtype=np.float64)
+    elif case["name"] == "topk_many_ties_low_index":
+        S = (np.arange(640) % 5).astype(np.float64)[None, :]
+    else:  # rule-built row
+        S = -np.arange(640, dtype=np.float64)[None, :]
+    nb = S.shape[1]
+    full = np.zeros((nb, nb))
+    full[: S.shape[0]] = S
+    tau = case.get("tau")
+    if isinstance(tau, str):
+        tau = float(tau)
+    r = O.route(full[None, None], tau=tau if tau is not None else 1.0,
+                topk_ratio=case.get("topk_ratio"), prefix_len=case.get("prefix_len", 0))
+    sel = r["sel"][0, 0]
+    if "expect" in case:
+        for a, want in enumerate(case["expect"]):
+            assert list(np.nonzero(sel[a])[0]) == want, (case["name"], a)
+    elif case["name"] == "topk_many_ties_low_index":
+        assert list(np.nonzero(sel[0])[0]) == [5 * j + 4 for j in range(64)]
+    else:
+        assert sel[0].sum() == case["expect_count"]
+
+
+def test_closed_form_centroid_case():
+    """Two blocks, D = 4, all content in dimension 0 (scale = 1/2).
+
+    Query rows alternate x in {0.5, 1.5} (block mean 1).  Block-0 keys
+    alternate {1, 3} (mean 2) with v = e_0; block-1 keys alternate {0, 1}
+    (mean 0.5) with v = 0.  Scores are 2 and 0.5: mean 1.25, std 0.75,
+    tau = 1 gives thr = 2, so block 0 is exact and block 1 goes through its
+    centroid.  Output dim 0 for a row with query x is E0 / (E0 + C1) with
+    E0 = 32 e^{x/2} + 32 e^{3x/2} and C1 = 64 e^{x/4} (log-mass log 64)."""
+    N, D = 128, 4
+    q = np.zeros((1, N, 1, D))
+    k = np.zeros((1, N, 1, D))
+    v = np.zeros((1, N, 1, D))
+    xs = np.where(np.arange(N) % 2 == 0, 0.5, 1.5)
+    q[0, :, 0, 0] = xs
+    k[0, :64, 0, 0] = np.where(np.arange(64) % 2 == 0, 1.0, 3.0)
+    k[0, 64:, 0, 0] = np.where(np.arange(64) % 2 == 0, 0.0, 1.0)
+    v[0, :64, 0, 0] = 1.0
+    out, info = O.forward(q, k, v, tau=1.0)
+    assert info["sel"][0, 0].tolist() == [[True, False], [True, False]]
+    E0 = 32 * np.exp(xs / 2) + 32 * np.exp(1.5 * xs)
+    C1 = 64 * np.exp(xs / 4)
+    np.testing.assert_allclose(out[0, :, 0, 0], E0 / (E0 + C1), rtol=1e-14, atol=0)
+    assert np.all(out[0, :, 0, 1:] == 0)
+
+
+# ------------------------------------------------------------------- invariants
+
+
+def test_tau_monotone_nesting():
+    q, k, v = inputs.clustered(1, 1024, 3, 64, seed=2)
+    qb, kb = O.pool(_f64(q)), O.pool(_f64(k))
+    S = O.block_scores(qb, kb)
+    prev = None
+    for tau in [-1.0, 0.0, 0.5, 1.0, 1.5, 3.0]:
+        sel = O.route(S, tau=tau)["sel"]
+        if prev is not None:
+            assert not (sel & ~prev).any()
+        prev = sel
+
+
+def test_topk_counts_with_sink():
+    q, k, v = _rand(1, 1000, 2, 64, seed=4)
+    S = O.block_scores(O.pool(q), O.pool(k))
+    nb = S.shape[-1]
+    r = O.route(S, topk_ratio=0.2, prefix_len=130)
+    kk = O.topk_count(0.2, nb)
+    pb = 3
+    sel = r["sel"]
+    assert sel[:, :, :pb].all()
+    for a in range(pb, nb):
+        cnt = sel[0, :, a].sum(axis=-1)
+        topk_only = O.route(S, topk_ratio=0.2)["sel"][0, :, a]
+        extra = (~topk_only[:, :pb]).sum(axis=-1)
+        np.testing.assert_array_equal(cnt, kk + extra)
+
+
+def test_output_inside_value_hull_and_prefix_rows_dense():
+    q, k, v = _rand(1, 300, 2, 64, seed=8)
+    out, _ = O.forward(q, k, v, tau=1.0, prefix_len=100)
+    lo = v.min(axis=1, keepdims=True)
+    hi = v.max(axis=1, keepdims=True)
+    assert (out >= lo - 1e-12).all() and (out <= hi + 1e-12).all()
+    dense = dense_reference(q, k, v)
+    np.testing.assert_allclose(out[:, :128], dense[:, :128], atol=1e-12)
+    assert np.abs(out[:, 128:] - dense[:, 128:]).max() > 1e-6
+
+
+def test_centroid_never_overcounts_block_mass():
+    """Jensen: n_c exp(q . kbar_c s) <= sum_j exp(q . k_j s).  With V = the
+    indicator of block c, output dim 0 is block c's share of the softmax mass,
+    which must not grow when c moves from the exact to the centroid path."""
+    q, k, v = _rand(1, 256, 1, 64, seed=12)
+    c = 2
+    v = np.zeros_like(v)
+    v[:, c * 64 : (c + 1) * 64, :, 0] = 1.0
+    nb = 4
+    exact = np.ones((1, 1, nb, nb), dtype=bool)
+    approx = exact.copy()
+    approx[..., c] = False
+    o_exact, _ = O.forward(q, k, v, mask=exact)
+    o_approx, _ = O.forward(q, k, v, mask=approx)
+    assert (o_approx[..., 0] <= o_exact[..., 0] + 1e-15).all()
+    assert (o_approx[..., 0] < o_exact[..., 0]).mean() > 0.99
+
+
+def test_block_permutation_equivariance():
+    q, k, v = inputs.clustered(1, 512, 2, 64, seed=6)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    out, info = O.forward(q, k, v, tau=1.0)
+    perm = np.array([3, 0, 7, 5, 1, 6, 2, 4])
+    rows = (perm[:, None] * 64 + np.arange(64)[None]).reshape(-1)
+    k2, v2 = k[:, rows], v[:, rows]
+    out2, info2 = O.forward(q, k2, v2, tau=1.0)
+    np.testing.assert_array_equal(info2["sel"], info["sel"][..., perm])
+    np.testing.assert_allclose(out2, out, atol=1e-12)
+
+
+def test_selection_lists_are_ascending():
+    q, k, v = _rand(1, 640, 2, 64, seed=1)
+    _, info = O.forward(q, k, v, tau=0.8)
+    lists, counts = O.selection_lists(info["sel"])
+    for h in range(2):
+        for a in range(10):
+            idx = lists[0, h, a, : counts[0, h, a]]
+            assert (np.diff(idx) > 0).all()
+            assert (lists[0, h, a, counts[0, h, a]:] == -1).all()
+
+
+def test_tiny_iid_density_is_about_one_sigma_tail():
+    """For i.i.d. inputs the scores of a row are roughly normal, so tau = 1
+    keeps about P(Z >= 1) = 0.159 of the blocks (a sanity range, not a pin)."""
+    w = inputs.make_workload("tiny")
+    q, k = _f64(w.q), _f64(w.k)
+    S = O.block_scores(O.pool(q), O.pool(k))
+    d = O.route(S, tau=1.0)["sel"].mean()
+    assert 0.10 < d < 0.22
+
+
+# ----------------------------------------------------------------- generators
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 37
+    x[:4] = [1.0 + 2**-8, 1.0 + 3 * 2**-8, -(1.0 + 2**-8), 0.0]  # ties
+    mine = inputs.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(mine, ref)
+
+
+def test_generators_are_seeded_and_shaped():
+    a = inputs.make_workload("tiny")
+    b = inputs.make_workload("tiny")
+    assert a.q.shape == (1, 1024, 2, 64) and a.q.dtype == np.uint16
+    np.testing.assert_array_equal(a.q, b.q)
+    c = inputs.clustered(1, 512, 2, 64, seed=1)
+    assert c[0] is c[1]  # Q = K
+    h = inputs.h3_joint(1, 1100, 2, 64, prefix_len=64, seed=4)
+    assert h[0].shape == (1, 1100, 2, 64)
+    assert not np.array_equal(h[0][:, :64], h[1][:, :64])  # independent prefix
+    np.testing.assert_array_equal(h[0][:, 64:], h[1][:, 64:])  # Q = K on video rows
