@@ -1,0 +1,356 @@
+"""ctypes binding of ``libsparse_attn.so`` (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels.  torch is
+used for device memory (inputs, output and workspace are torch tensors) and
+for the current HIP stream, whose handle is passed to the library.  If the
+library has not been built this module raises on first use; there is no
+other implementation to fall back to.
+
+The C declarations, argument meanings and error behaviour are documented in
+``include/sparse_attn.h``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional, Tuple
+
+__all__ = [
+    "SparseAttnError",
+    "SparseAttnPlan",
+    "sparse_attn",
+    "load_library",
+    "library_path",
+    "SA_ROUTE_TAU",
+    "SA_ROUTE_TOPK",
+    "SA_FLAG_CENTROID",
+    "SA_FLAG_LOGMASS",
+]
+
+SA_ROUTE_TAU = 0
+SA_ROUTE_TOPK = 1
+SA_FLAG_CENTROID = 1
+SA_FLAG_LOGMASS = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libsparse_attn.so"
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str, message: str):
+        super().__init__(f"{where}: {message} ({code}): {detail}")
+        self.code = code
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("N", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("in_stride_b", ctypes.c_int64),
+        ("in_stride_t", ctypes.c_int64),
+        ("in_stride_h", ctypes.c_int64),
+        ("out_stride_b", ctypes.c_int64),
+        ("out_stride_t", ctypes.c_int64),
+        ("out_stride_h", ctypes.c_int64),
+        ("route", ctypes.c_int32),
+        ("tau", ctypes.c_float),
+        ("topk_ratio", ctypes.c_float),
+        ("prefix_len", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [
+        ("total_bytes", ctypes.c_uint64),
+        ("qbar", ctypes.c_uint64),
+        ("kbar", ctypes.c_uint64),
+        ("vbar", ctypes.c_uint64),
+        ("kbar_bf16", ctypes.c_uint64),
+        ("vbar_bf16", ctypes.c_uint64),
+        ("counts", ctypes.c_uint64),
+        ("lists", ctypes.c_uint64),
+        ("n_blocks", ctypes.c_int32),
+        ("n_blocks_padded", ctypes.c_int32),
+        ("tail_rows", ctypes.c_int32),
+        ("prefix_blocks", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("dense", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return os.environ.get("SPARSE_ATTN_LIB", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the built library once; raise if it is missing."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(
+                f"{path} not found: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()' or "
+                "python -m block_sparse_video_fp32_amd.build)"
+            )
+        lib = ctypes.CDLL(path)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        lib.sparse_attn_plan_create.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(vp)]
+        lib.sparse_attn_plan_create.restype = i32
+        lib.sparse_attn_plan_destroy.argtypes = [vp]
+        lib.sparse_attn_plan_destroy.restype = None
+        lib.sparse_attn_workspace_layout.argtypes = [vp, ctypes.POINTER(_Layout)]
+        lib.sparse_attn_workspace_layout.restype = i32
+        lib.sparse_attn_forward.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.sparse_attn_forward.restype = i32
+        lib.sparse_attn_pool.argtypes = [vp, vp, vp, vp, vp, sz, vp]
+        lib.sparse_attn_pool.restype = i32
+        lib.sparse_attn_select.argtypes = [vp, vp, sz, vp]
+        lib.sparse_attn_select.restype = i32
+        lib.sparse_attn_attend.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.sparse_attn_attend.restype = i32
+        lib.sparse_attn_strerror.argtypes = [i32]
+        lib.sparse_attn_strerror.restype = ctypes.c_char_p
+        lib.sparse_attn_last_error.argtypes = []
+        lib.sparse_attn_last_error.restype = ctypes.c_char_p
+        lib.sparse_attn_abi_version.argtypes = []
+        lib.sparse_attn_abi_version.restype = i32
+        _lib = lib
+        return lib
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        lib = load_library()
+        raise SparseAttnError(
+            rc,
+            where,
+            lib.sparse_attn_last_error().decode(),
+            lib.sparse_attn_strerror(rc).decode(),
+        )
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream_handle(device) -> int:
+    import torch
+
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+class SparseAttnPlan:
+    """A validated shape + routing configuration (host object).
+
+    ``tau=-inf`` selects the dense path.  Exactly one of ``tau`` and
+    ``topk_ratio`` is used: ``topk_ratio`` wins when given.
+    """
+
+    def __init__(
+        self,
+        B: int,
+        N: int,
+        H: int,
+        D: int,
+        *,
+        tau: Optional[float] = 1.0,
+        topk_ratio: Optional[float] = None,
+        prefix_len: int = 0,
+        centroid: bool = True,
+        logmass: bool = True,
+        sm_scale: Optional[float] = None,
+        in_strides: Optional[Tuple[int, int, int]] = None,
+        out_strides: Optional[Tuple[int, int, int]] = None,
+    ):
+        lib = load_library()
+        p = _Params()
+        p.B, p.N, p.H, p.D = int(B), int(N), int(H), int(D)
+        if in_strides is not None:
+            p.in_stride_b, p.in_stride_t, p.in_stride_h = (int(x) for x in in_strides)
+        if out_strides is not None:
+            p.out_stride_b, p.out_stride_t, p.out_stride_h = (int(x) for x in out_strides)
+        if topk_ratio is not None:
+            p.route = SA_ROUTE_TOPK
+            p.topk_ratio = float(topk_ratio)
+            p.tau = 0.0
+        else:
+            p.route = SA_ROUTE_TAU
+            p.tau = float(1.0 if tau is None else tau)
+        p.prefix_len = int(prefix_len)
+        p.sm_scale = float(sm_scale) if sm_scale else 0.0
+        p.flags = (SA_FLAG_CENTROID if centroid else 0) | (SA_FLAG_LOGMASS if logmass else 0)
+        handle = ctypes.c_void_p()
+        _check(lib.sparse_attn_plan_create(ctypes.byref(p), ctypes.byref(handle)), "sparse_attn_plan_create")
+        self._lib = lib
+        self._h = handle
+        self.params = p
+        lay = _Layout()
+        _check(lib.sparse_attn_workspace_layout(handle, ctypes.byref(lay)), "sparse_attn_workspace_layout")
+        self.layout = {name: getattr(lay, name) for name, _ in _Layout._fields_}
+        self.shape = (p.B, p.N, p.H, p.D)
+        self._ws = {}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.sparse_attn_plan_destroy(h)
+            self._h = None
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self.layout["total_bytes"])
+
+    @property
+    def dense(self) -> bool:
+        return bool(self.layout["dense"])
+
+    def workspace(self, device):
+        """A cached device workspace for this plan (torch uint8 tensor)."""
+        import torch
+
+        key = str(torch.device(device))
+        ws = self._ws.get(key)
+        if ws is None:
+            ws = torch.empty(max(256, self.workspace_bytes), dtype=torch.uint8, device=device)
+            self._ws[key] = ws
+        return ws
+
+    # -- argument checks (marshalling only) --------------------------------
+    def _check_io(self, *ts):
+        import torch
+
+        for t in ts:
+            if t is None:
+                continue
+            if t.dtype != torch.bfloat16:
+                raise TypeError("q, k, v and out must be torch.bfloat16")
+            if tuple(t.shape) != self.shape:
+                raise ValueError(f"tensor shape {tuple(t.shape)} != plan shape {self.shape}")
+            if t.stride(3) != 1:
+                raise ValueError("the head dimension must be contiguous")
+            if t.device.type != "cuda":
+                raise ValueError("tensors must live on a HIP device")
+
+    def _call(self, fn, name, device, *args):
+        import torch
+
+        with torch.cuda.device(device):
+            _check(fn(self._h, *args, ctypes.c_void_p(_stream_handle(device))), name)
+
+    def forward(self, q, k, v, out=None, ws=None):
+        import torch
+
+        if out is None:
+            out = torch.empty_like(q)
+        self._check_io(q, k, v, out)
+        ws = self.workspace(q.device) if ws is None else ws
+        self._call(self._lib.sparse_attn_forward, "sparse_attn_forward", q.device,
+                   _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws), ws.numel())
+        return out
+
+    def pool(self, q, k, v, ws=None):
+        self._check_io(q, k, v)
+        ws = self.workspace(q.device) if ws is None else ws
+        self._call(self._lib.sparse_attn_pool, "sparse_attn_pool", q.device,
+                   _ptr(q), _ptr(k), _ptr(v), _ptr(ws), ws.numel())
+        return ws
+
+    def select(self, ws):
+        self._call(self._lib.sparse_attn_select, "sparse_attn_select", ws.device, _ptr(ws), ws.numel())
+        return ws
+
+    def attend(self, q, k, v, out, ws):
+        self._check_io(q, k, v, out)
+        self._call(self._lib.sparse_attn_attend, "sparse_attn_attend", q.device,
+                   _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws), ws.numel())
+        return out
+
+    # -- workspace views -----------------------------------------------------
+    def _view(self, ws, name, dtype, shape):
+        import torch
+
+        off = int(self.layout[name])
+        nbytes = int(torch.tensor([], dtype=dtype).element_size())
+        for s in shape:
+            nbytes *= s
+        return ws[off : off + nbytes].view(dtype).view(*shape)
+
+    def route_views(self, ws):
+        """(counts [B,H,n_b] int32, lists [B,H,n_b,n_b] int32) inside ws."""
+        import torch
+
+        B, N, H, D = self.shape
+        nb = self.layout["n_blocks"]
+        counts = self._view(ws, "counts", torch.int32, (B, H, nb))
+        lists = self._view(ws, "lists", torch.int32, (B, H, nb, nb))
+        return counts, lists
+
+    def pooled_views(self, ws):
+        """fp32 (qbar, kbar, vbar) [B,H,n_b,D] and bf16 (kbar16, vbar16) [B,H,n_bp,D]."""
+        import torch
+
+        B, N, H, D = self.shape
+        nb, nbp = self.layout["n_blocks"], self.layout["n_blocks_padded"]
+        f = [self._view(ws, n, torch.float32, (B, H, nb, D)) for n in ("qbar", "kbar", "vbar")]
+        b = [self._view(ws, n, torch.bfloat16, (B, H, nbp, D)) for n in ("kbar_bf16", "vbar_bf16")]
+        return (*f, *b)
+
+
+def sparse_attn(
+    q,
+    k,
+    v,
+    *,
+    tau: Optional[float] = None,
+    topk_ratio: Optional[float] = None,
+    prefix_len: int = 0,
+    centroid: bool = True,
+    logmass: bool = True,
+    sm_scale: Optional[float] = None,
+    out=None,
+    return_route: bool = False,
+):
+    """Routed block-sparse attention of bf16 BTHD tensors ``[B, N, H, D]``.
+
+    ``tau`` (default 1.0) or ``topk_ratio`` picks the routing; ``tau=-inf``
+    is the dense path.  With ``return_route`` the per-query-block counts and
+    index lists are returned as well (views into the workspace).
+    """
+    import torch
+
+    B, N, H, D = q.shape
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    plan = SparseAttnPlan(
+        B, N, H, D,
+        tau=1.0 if (tau is None and topk_ratio is None) else tau,
+        topk_ratio=topk_ratio,
+        prefix_len=prefix_len,
+        centroid=centroid,
+        logmass=logmass,
+        sm_scale=sm_scale,
+        in_strides=(q.stride(0), q.stride(1), q.stride(2)),
+        out_strides=(out.stride(0), out.stride(1), out.stride(2)),
+    )
+    if not (k.stride() == q.stride() and v.stride() == q.stride()):
+        raise ValueError("q, k and v must share strides")
+    ws = plan.workspace(q.device)
+    plan.forward(q, k, v, out=out, ws=ws)
+    if return_route:
+        counts, lists = plan.route_views(ws)
+        return out, counts, lists
+    return out

@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI host layer (sparse_attn_api.cpp) and
+// the gfx950 kernels (sparse_attn_kernels.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace sa {
+
+constexpr int kBlock = 64;
+
+// Everything a launch needs, derived once by the plan.
+struct Shape {
+  int B, N, H, D;
+  long long isb, ist, ish;  // q/k/v element strides (d-stride 1)
+  long long osb, ost, osh;  // out element strides
+  int nb;                   // n_b = ceil(N / 64)
+  int nbp;                  // n_b rounded up to 64
+  int tail;                 // rows of block nb - 1
+  int pb;                   // prefix blocks, <= nb
+  int route;                // SA_ROUTE_TAU / SA_ROUTE_TOPK
+  int topk;                 // k for top-K routing
+  int dense;                // tau = -inf
+  float tau;
+  float c1;                 // softmax scale * log2(e)
+  float bias_full;          // log2(64) when the log-mass bias is on, else 0
+  float bias_tail;          // log2(tail) when on, else 0
+  int centroid;             // centroid terms on
+};
+
+struct Workspace {
+  float* qbar;
+  float* kbar;
+  float* vbar;
+  uint16_t* kbar16;
+  uint16_t* vbar16;
+  int* counts;
+  int* lists;
+};
+
+hipError_t launch_pool(const Shape& s, const void* q, const void* k, const void* v,
+                       const Workspace& ws, hipStream_t stream);
+hipError_t launch_select(const Shape& s, const Workspace& ws, hipStream_t stream);
+hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v, void* out,
+                         const Workspace& ws, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,310 @@
+// C-ABI host layer: parameter validation, plans, workspace layout, device
+// check and the launch sequence.  The declarations and their contracts are
+// in include/sparse_attn.h.
+#include "sparse_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "sa_internal.h"
+
+struct sparse_attn_plan {
+  sparse_attn_params params;
+  sa::Shape shape;
+  sparse_attn_ws_layout layout;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SA_OK;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device result of the architecture check, filled on first use.
+std::mutex g_dev_mu;
+std::vector<int> g_dev_ok;            // 0 unknown, 1 gfx950, -1 other
+std::vector<std::string> g_dev_arch;  // arch name as reported
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(SA_EUNSUPPORTED_DEVICE, "requires gfx950, found no HIP device (%s)",
+                hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if ((int)g_dev_ok.size() <= dev) {
+    g_dev_ok.resize(dev + 1, 0);
+    g_dev_arch.resize(dev + 1);
+  }
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(SA_EUNSUPPORTED_DEVICE, "requires gfx950, device %d not queryable (%s)", dev,
+                  hipGetErrorString(e));
+    const char* name = prop.gcnArchName;
+    g_dev_arch[dev] = name;
+    g_dev_ok[dev] = (std::strncmp(name, "gfx950", 6) == 0 && (name[6] == 0 || name[6] == ':')) ? 1 : -1;
+  }
+  if (g_dev_ok[dev] != 1)
+    return fail(SA_EUNSUPPORTED_DEVICE, "requires gfx950, found %s (device %d)",
+                g_dev_arch[dev].c_str(), dev);
+  return SA_OK;
+}
+
+int check_strides(const char* what, int64_t sb, int64_t st, int64_t sh) {
+  if (sb <= 0 || st <= 0 || sh <= 0)
+    return fail(SA_EINVAL, "%s strides must all be positive (or all zero for contiguous BTHD)", what);
+  if ((sb % 8) || (st % 8) || (sh % 8))
+    return fail(SA_EALIGN, "%s strides must be multiples of 8 elements (16 bytes)", what);
+  return SA_OK;
+}
+
+int validate_params(const sparse_attn_params& p) {
+  if (p.B < 1 || p.N < 1 || p.H < 1)
+    return fail(SA_EINVAL, "B, N and H must be >= 1 (got B=%d N=%d H=%d)", p.B, p.N, p.H);
+  if (p.D != 64 && p.D != 128)
+    return fail(SA_EUNSUPPORTED_SHAPE, "head dim D must be 64 or 128 (got %d)", p.D);
+  const int64_t nb = (int64_t(p.N) + sa::kBlock - 1) / sa::kBlock;
+  if (nb > SA_MAX_BLOCKS)
+    return fail(SA_EUNSUPPORTED_SHAPE, "N=%d gives %lld blocks, more than %d", p.N, (long long)nb,
+                SA_MAX_BLOCKS);
+  if ((int64_t)p.B * p.H * nb > (int64_t)1 << 30)
+    return fail(SA_EUNSUPPORTED_SHAPE, "B*H*n_b too large");
+  const bool in0 = p.in_stride_b == 0 && p.in_stride_t == 0 && p.in_stride_h == 0;
+  const bool out0 = p.out_stride_b == 0 && p.out_stride_t == 0 && p.out_stride_h == 0;
+  int rc;
+  if (!in0 && (rc = check_strides("input", p.in_stride_b, p.in_stride_t, p.in_stride_h))) return rc;
+  if (!out0 && (rc = check_strides("output", p.out_stride_b, p.out_stride_t, p.out_stride_h))) return rc;
+  if (p.route == SA_ROUTE_TAU) {
+    if (std::isnan(p.tau)) return fail(SA_EINVAL, "tau must not be NaN");
+  } else if (p.route == SA_ROUTE_TOPK) {
+    if (!(p.topk_ratio > 0.0f && p.topk_ratio <= 1.0f))
+      return fail(SA_EINVAL, "topk_ratio must be in (0, 1] (got %g)", (double)p.topk_ratio);
+  } else {
+    return fail(SA_EINVAL, "route must be SA_ROUTE_TAU or SA_ROUTE_TOPK (got %d)", p.route);
+  }
+  if (p.prefix_len < 0 || p.prefix_len > p.N)
+    return fail(SA_EINVAL, "prefix_len must be in [0, N] (got %d, N=%d)", p.prefix_len, p.N);
+  if (!std::isfinite(p.sm_scale)) return fail(SA_EINVAL, "sm_scale must be finite");
+  if (p.flags & ~(SA_FLAG_CENTROID | SA_FLAG_LOGMASS))
+    return fail(SA_EINVAL, "unknown flag bits 0x%x", p.flags);
+  return SA_OK;
+}
+
+void build_plan(sparse_attn_plan* pl) {
+  const sparse_attn_params& p = pl->params;
+  sa::Shape& s = pl->shape;
+  s.B = p.B;
+  s.N = p.N;
+  s.H = p.H;
+  s.D = p.D;
+  const bool in0 = p.in_stride_b == 0 && p.in_stride_t == 0 && p.in_stride_h == 0;
+  const bool out0 = p.out_stride_b == 0 && p.out_stride_t == 0 && p.out_stride_h == 0;
+  const long long hd = (long long)p.H * p.D;
+  s.isb = in0 ? hd * p.N : p.in_stride_b;
+  s.ist = in0 ? hd : p.in_stride_t;
+  s.ish = in0 ? p.D : p.in_stride_h;
+  s.osb = out0 ? hd * p.N : p.out_stride_b;
+  s.ost = out0 ? hd : p.out_stride_t;
+  s.osh = out0 ? p.D : p.out_stride_h;
+  s.nb = (p.N + sa::kBlock - 1) / sa::kBlock;
+  s.nbp = (s.nb + 63) / 64 * 64;
+  s.tail = p.N - sa::kBlock * (s.nb - 1);
+  s.pb = (p.prefix_len + sa::kBlock - 1) / sa::kBlock;
+  if (s.pb > s.nb) s.pb = s.nb;
+  s.route = p.route;
+  s.tau = p.tau;
+  s.dense = (p.route == SA_ROUTE_TAU && std::isinf(p.tau) && p.tau < 0) ? 1 : 0;
+  s.topk = 0;
+  if (p.route == SA_ROUTE_TOPK) {
+    // k = clamp(ceil(r * n_b - 1e-6), 1, n_b) with r the float32 ratio.
+    double k = std::ceil((double)p.topk_ratio * s.nb - 1e-6);
+    if (k < 1) k = 1;
+    if (k > s.nb) k = s.nb;
+    s.topk = (int)k;
+  }
+  const double scale = p.sm_scale > 0.0f ? (double)p.sm_scale : 1.0 / std::sqrt((double)p.D);
+  s.c1 = (float)(scale * 1.4426950408889634);  // log2(e)
+  const bool logmass = (p.flags & SA_FLAG_LOGMASS) != 0;
+  s.bias_full = logmass ? 6.0f : 0.0f;  // log2(64)
+  s.bias_tail = logmass ? (float)std::log2((double)s.tail) : 0.0f;
+  s.centroid = (p.flags & SA_FLAG_CENTROID) ? 1 : 0;
+
+  sparse_attn_ws_layout& L = pl->layout;
+  std::memset(&L, 0, sizeof(L));
+  const uint64_t bh = (uint64_t)p.B * p.H;
+  const uint64_t pooled = bh * s.nb * p.D * sizeof(float);
+  const uint64_t pooled16 = bh * s.nbp * p.D * sizeof(uint16_t);
+  uint64_t off = 0;
+  L.qbar = off; off = align256(off + pooled);
+  L.kbar = off; off = align256(off + pooled);
+  L.vbar = off; off = align256(off + pooled);
+  L.kbar_bf16 = off; off = align256(off + pooled16);
+  L.vbar_bf16 = off; off = align256(off + pooled16);
+  L.counts = off; off = align256(off + bh * s.nb * sizeof(int32_t));
+  L.lists = off; off = align256(off + bh * s.nb * (uint64_t)s.nb * sizeof(int32_t));
+  L.total_bytes = off;
+  L.n_blocks = s.nb;
+  L.n_blocks_padded = s.nbp;
+  L.tail_rows = s.tail;
+  L.prefix_blocks = s.pb;
+  L.topk = s.topk;
+  L.dense = s.dense;
+}
+
+sa::Workspace carve(const sparse_attn_plan* pl, void* ws) {
+  char* base = static_cast<char*>(ws);
+  const sparse_attn_ws_layout& L = pl->layout;
+  sa::Workspace w;
+  w.qbar = reinterpret_cast<float*>(base + L.qbar);
+  w.kbar = reinterpret_cast<float*>(base + L.kbar);
+  w.vbar = reinterpret_cast<float*>(base + L.vbar);
+  w.kbar16 = reinterpret_cast<uint16_t*>(base + L.kbar_bf16);
+  w.vbar16 = reinterpret_cast<uint16_t*>(base + L.vbar_bf16);
+  w.counts = reinterpret_cast<int*>(base + L.counts);
+  w.lists = reinterpret_cast<int*>(base + L.lists);
+  return w;
+}
+
+int check_ws(const sparse_attn_plan* pl, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(SA_EINVAL, "workspace pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u)
+    return fail(SA_EALIGN, "workspace must be 256-byte aligned");
+  if (ws_bytes < pl->layout.total_bytes)
+    return fail(SA_EWORKSPACE, "workspace has %zu bytes, plan needs %llu", ws_bytes,
+                (unsigned long long)pl->layout.total_bytes);
+  return SA_OK;
+}
+
+int check_tensors(const void* q, const void* k, const void* v, const void* out, bool need_out) {
+  if (!q || !k || !v || (need_out && !out)) return fail(SA_EINVAL, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (need_out && !aligned16(out)))
+    return fail(SA_EALIGN, "q, k, v and out must be 16-byte aligned");
+  return SA_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SA_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_abi_version(void) { return SA_ABI_VERSION; }
+
+const char* sparse_attn_strerror(int code) {
+  switch (code) {
+    case SA_OK: return "success";
+    case SA_EINVAL: return "invalid argument";
+    case SA_EUNSUPPORTED_SHAPE: return "unsupported shape";
+    case SA_EUNSUPPORTED_DEVICE: return "unsupported device (requires gfx950)";
+    case SA_EWORKSPACE: return "workspace too small";
+    case SA_EALIGN: return "misaligned pointer or stride";
+    case SA_ELAUNCH: return "kernel launch failed";
+    default: return "unknown error";
+  }
+}
+
+const char* sparse_attn_last_error(void) { return g_last_error.c_str(); }
+
+int sparse_attn_plan_create(const sparse_attn_params* params, sparse_attn_plan** plan) {
+  if (!plan) return fail(SA_EINVAL, "plan output pointer is NULL");
+  *plan = nullptr;
+  if (!params) return fail(SA_EINVAL, "params is NULL");
+  int rc = validate_params(*params);
+  if (rc) return rc;
+  sparse_attn_plan* pl = new (std::nothrow) sparse_attn_plan;
+  if (!pl) return fail(SA_EINVAL, "out of host memory");
+  pl->params = *params;
+  build_plan(pl);
+  *plan = pl;
+  return ok();
+}
+
+void sparse_attn_plan_destroy(sparse_attn_plan* plan) { delete plan; }
+
+int sparse_attn_workspace_layout(const sparse_attn_plan* plan, sparse_attn_ws_layout* layout) {
+  if (!plan || !layout) return fail(SA_EINVAL, "plan and layout must be non-NULL");
+  *layout = plan->layout;
+  return ok();
+}
+
+int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(SA_EINVAL, "plan is NULL");
+  int rc;
+  if ((rc = check_tensors(q, k, v, nullptr, false))) return rc;
+  if ((rc = check_ws(plan, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  if ((rc = launched(sa::launch_pool(plan->shape, q, k, v, carve(plan, ws), (hipStream_t)stream), "pool")))
+    return rc;
+  return ok();
+}
+
+int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(SA_EINVAL, "plan is NULL");
+  int rc;
+  if ((rc = check_ws(plan, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  if ((rc = launched(sa::launch_select(plan->shape, carve(plan, ws), (hipStream_t)stream), "select")))
+    return rc;
+  return ok();
+}
+
+int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
+                       void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(SA_EINVAL, "plan is NULL");
+  int rc;
+  if ((rc = check_tensors(q, k, v, out, true))) return rc;
+  if ((rc = check_ws(plan, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  if ((rc = launched(sa::launch_attend(plan->shape, q, k, v, out, carve(plan, ws), (hipStream_t)stream),
+                     "attend")))
+    return rc;
+  return ok();
+}
+
+int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
+                        void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(SA_EINVAL, "plan is NULL");
+  int rc;
+  if ((rc = check_tensors(q, k, v, out, true))) return rc;
+  if ((rc = check_ws(plan, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  const sa::Workspace w = carve(plan, ws);
+  hipStream_t st = (hipStream_t)stream;
+  if (!plan->shape.dense) {
+    if ((rc = launched(sa::launch_pool(plan->shape, q, k, v, w, st), "pool"))) return rc;
+    if ((rc = launched(sa::launch_select(plan->shape, w, st), "select"))) return rc;
+  }
+  if ((rc = launched(sa::launch_attend(plan->shape, q, k, v, out, w, st), "attend"))) return rc;
+  return ok();
+}
+
+}  // extern "C"

@@ -109,38 +109,73 @@ class Workload:
         )
 
 
+def _bf16(x) -> np.ndarray:
+    """float32 (numpy or torch) -> bf16 bit patterns, round to nearest even.
+
+    torch's float32 -> bfloat16 cast rounds to nearest even (checked against
+    ``f32_to_bf16_bits`` in the tests) and runs on all host threads."""
+    import torch
+
+    t = x if isinstance(x, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
 def iid(B: int, N: int, H: int, D: int, seed: int):
     """Q, K, V i.i.d. N(0,1), drawn in that order, rounded to bf16."""
     rng = np.random.Generator(np.random.PCG64(seed))
     out = []
     for _ in range(3):
-        out.append(f32_to_bf16_bits(rng.standard_normal((B, N, H, D), dtype=np.float32)))
+        out.append(_bf16(rng.standard_normal((B, N, H, D), dtype=np.float32)))
     return tuple(out)
 
 
-def _smooth_1d(rng, B, N, H, D, chunk=2048):
+def _sum_of_sines(ang_fn, rows, H, D, chunk=1024):
+    """(1/sqrt 2) * sum_j sin(angle[t, h, d, j]) for t < rows, float32 [rows, H, D].
+
+    The elementwise math runs in torch (float64, all host threads); the
+    random draws stay with numpy's PCG64 generator."""
+    import torch
+
+    s = np.empty((rows, H, D), dtype=np.float32)
+    for t0 in range(0, rows, chunk):
+        t1 = min(rows, t0 + chunk)
+        ang = ang_fn(torch.arange(t0, t1, dtype=torch.int64))
+        s[t0:t1] = (torch.sin(ang).sum(dim=-1) / math.sqrt(2.0)).to(torch.float32).numpy()
+    return s
+
+
+def _smooth_1d(rng, B, N, H, D):
+    import torch
+
     periods = np.exp(rng.uniform(math.log(256.0), math.log(4096.0), size=(H, D, 4)))
-    phases = rng.uniform(0.0, 2.0 * math.pi, size=(H, D, 4))
-    omega = 2.0 * math.pi / periods  # [H, D, 4]
-    s = np.empty((N, H, D), dtype=np.float32)
-    for t0 in range(0, N, chunk):
-        t = np.arange(t0, min(N, t0 + chunk), dtype=np.float64)
-        ang = t[:, None, None, None] * omega[None] + phases[None]
-        s[t0 : t0 + len(t)] = (np.sin(ang).sum(axis=-1) / math.sqrt(2.0)).astype(np.float32)
-    return np.broadcast_to(s[None], (B, N, H, D))
+    phases = torch.from_numpy(rng.uniform(0.0, 2.0 * math.pi, size=(H, D, 4)))
+    omega = torch.from_numpy(2.0 * math.pi / periods)  # [H, D, 4]
+
+    def ang(t):
+        return t.to(torch.float64)[:, None, None, None] * omega[None] + phases[None]
+
+    return _sum_of_sines(ang, N, H, D)
+
+
+def _signal_plus_noise(rng, s, B):
+    """bf16(1.5 s + N(0,1)) with s [rows, H, D] shared by every batch entry."""
+    import torch
+
+    rows, H, D = s.shape
+    noise = torch.from_numpy(rng.standard_normal((B, rows, H, D), dtype=np.float32))
+    return _bf16(noise.add_(torch.from_numpy(s)[None], alpha=1.5))
 
 
 def clustered(B: int, N: int, H: int, D: int, seed: int):
     """Q = K = 1.5 s(t) + N(0,1), V = N(0,1); s is a smooth per-head signal."""
     rng = np.random.Generator(np.random.PCG64(seed))
     s = _smooth_1d(rng, B, N, H, D)
-    qk = 1.5 * s + rng.standard_normal((B, N, H, D), dtype=np.float32)
-    q = f32_to_bf16_bits(qk.astype(np.float32))
-    v = f32_to_bf16_bits(rng.standard_normal((B, N, H, D), dtype=np.float32))
+    q = _signal_plus_noise(rng, s, B)
+    v = _bf16(rng.standard_normal((B, N, H, D), dtype=np.float32))
     return q, q, v
 
 
-def h3_joint(B: int, N: int, H: int, D: int, prefix_len: int, seed: int, chunk=2048):
+def h3_joint(B: int, N: int, H: int, D: int, prefix_len: int, seed: int):
     """Packed joint sequence: an i.i.d. prefix, then a frames x 24 x 42 video grid."""
     rng = np.random.Generator(np.random.PCG64(seed))
     P = prefix_len
@@ -148,27 +183,24 @@ def h3_joint(B: int, N: int, H: int, D: int, prefix_len: int, seed: int, chunk=2
     nvid = N - P
     per = [np.exp(rng.uniform(math.log(2.0), math.log(32.0), size=(H, D, 4))) for _ in range(3)]
     phases = rng.uniform(0.0, 2.0 * math.pi, size=(H, D, 4))
-    inv_f, inv_y, inv_x = (1.0 / p for p in per)
-    s = np.empty((nvid, H, D), dtype=np.float32)
+    import torch
+
+    inv = [torch.from_numpy(1.0 / p) for p in per]
+    ph = torch.from_numpy(phases)
     frame = _GRID_H * _GRID_W
-    for t0 in range(0, nvid, chunk):
-        t = np.arange(t0, min(nvid, t0 + chunk))
-        f = (t // frame).astype(np.float64)
-        y = ((t % frame) // _GRID_W).astype(np.float64)
-        x = (t % _GRID_W).astype(np.float64)
-        ang = 2.0 * math.pi * (
-            f[:, None, None, None] * inv_f[None]
-            + y[:, None, None, None] * inv_y[None]
-            + x[:, None, None, None] * inv_x[None]
-        ) + phases[None]
-        s[t0 : t0 + len(t)] = (np.sin(ang).sum(axis=-1) / math.sqrt(2.0)).astype(np.float32)
-    qk_vid = 1.5 * np.broadcast_to(s[None], (B, nvid, H, D)) + rng.standard_normal(
-        (B, nvid, H, D), dtype=np.float32
-    )
-    v_vid = rng.standard_normal((B, nvid, H, D), dtype=np.float32)
-    q = f32_to_bf16_bits(np.concatenate([pre[0], qk_vid.astype(np.float32)], axis=1))
-    k = f32_to_bf16_bits(np.concatenate([pre[1], qk_vid.astype(np.float32)], axis=1))
-    v = f32_to_bf16_bits(np.concatenate([pre[2], v_vid], axis=1))
+
+    def ang(t):
+        f = (t // frame).to(torch.float64)[:, None, None, None]
+        y = ((t % frame) // _GRID_W).to(torch.float64)[:, None, None, None]
+        x = (t % _GRID_W).to(torch.float64)[:, None, None, None]
+        return 2.0 * math.pi * (f * inv[0][None] + y * inv[1][None] + x * inv[2][None]) + ph[None]
+
+    s = _sum_of_sines(ang, nvid, H, D)
+    qk_vid = _signal_plus_noise(rng, s, B)
+    v_vid = _bf16(rng.standard_normal((B, nvid, H, D), dtype=np.float32))
+    q = np.concatenate([_bf16(pre[0]), qk_vid], axis=1)
+    k = np.concatenate([_bf16(pre[1]), qk_vid], axis=1)
+    v = np.concatenate([_bf16(pre[2]), v_vid], axis=1)
     return q, k, v
 
 

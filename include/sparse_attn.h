@@ -1,0 +1,165 @@
+/*
+ * sparse_attn.h -- C ABI of routed block-sparse attention for AMD MI355X.
+ *
+ * The method (Sol-style routing, as the Star7 "MiniMax H3 Activation Chunk &
+ * Attention Acceleration" README describes it in section 工作原理 > Sol, and
+ * the thakicloud "MiniMax-H3 ComfyUI accel stack" post in section
+ * 이 기술은 무엇인가):
+ *   1. Q, K and V are mean-pooled per 64-row block in FP32;
+ *   2. every query block a is scored against every key block c with
+ *      S[a][c] = Qbar_a . Kbar_c;
+ *   3. key blocks are selected per query block either by a threshold
+ *      S >= mean_a + tau * std_a (population std over all key blocks) or by
+ *      a top-K ratio (comfyui-wiki "Spark-H3" news, 워크플로 section); key
+ *      blocks holding rows of the packed prefix are always selected (exact KV
+ *      sink) and query blocks holding prefix rows attend densely (Star7
+ *      README, Sol; aikraft.ru Sol-Attn news, exact_kv_and_rows);
+ *   4. selected blocks are attended exactly (bf16 QK^T and PV on MFMA);
+ *      every unselected block contributes once through its centroid,
+ *      logit q_i . Kbar_c * scale + log(n_c), value Vbar_c, where n_c is the
+ *      block's valid row count (log-mass bias, "Spark-H3" news,
+ *      Spark-Reweight bullet); both kinds of term share one FP32 online
+ *      softmax.
+ *
+ * Tensors are bf16 in the BTHD layout [B, N, H, D] with D contiguous (the
+ * layout of the aikraft.ru RTX 5090 table), D in {64, 128}.  A ragged last
+ * block (N not a multiple of 64) holds N - 64 (n_b - 1) rows.
+ *
+ * Ownership: the caller owns every device buffer (q, k, v, out, workspace).
+ * The library never allocates or frees device memory and never synchronises:
+ * each call only enqueues kernels on the given HIP stream and returns.  A
+ * plan is host memory owned by the library from sparse_attn_plan_create to
+ * sparse_attn_plan_destroy; it may be reused for any number of calls with
+ * the same shape and parameters, from any thread.
+ *
+ * Errors: every entry point returns 0 on success or a negative SA_E* code.
+ * Host-detectable errors (bad arguments, wrong device, small workspace) are
+ * reported before anything is launched.  sparse_attn_last_error() returns a
+ * thread-local message for the last failing call on the calling thread.
+ * There is no fallback: an unsupported device or shape is an error.  NaN or
+ * Inf inputs are not checked; they propagate to the output.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_BLOCK 64          /* rows per query / key block */
+#define SA_MAX_BLOCKS 2048   /* largest supported n_b = ceil(N / 64) */
+#define SA_ABI_VERSION 1
+
+/* Routing modes (sparse_attn_params.route). */
+#define SA_ROUTE_TAU 0   /* S >= mean + tau * std; tau = -inf is the dense path */
+#define SA_ROUTE_TOPK 1  /* keep k = clamp(ceil(r * n_b - 1e-6), 1, n_b) blocks */
+
+/* Flags (sparse_attn_params.flags). */
+#define SA_FLAG_CENTROID 1u /* unselected blocks contribute through centroids */
+#define SA_FLAG_LOGMASS 2u  /* add log(n_c) to every centroid logit */
+#define SA_FLAGS_DEFAULT (SA_FLAG_CENTROID | SA_FLAG_LOGMASS)
+
+/* Error codes. */
+#define SA_OK 0
+#define SA_EINVAL (-1)              /* null pointer, bad parameter value */
+#define SA_EUNSUPPORTED_SHAPE (-2)  /* D not 64/128, n_b > SA_MAX_BLOCKS, ... */
+#define SA_EUNSUPPORTED_DEVICE (-3) /* current device is not gfx950 */
+#define SA_EWORKSPACE (-4)          /* workspace smaller than required */
+#define SA_EALIGN (-5)              /* pointer or stride not 16-byte aligned */
+#define SA_ELAUNCH (-6)             /* a HIP launch or runtime call failed */
+
+typedef struct sparse_attn_params {
+  int32_t B, N, H, D;
+  /* Element strides of q, k and v (which share them) and of out.  The
+   * d-stride is 1.  All three zero means contiguous BTHD:
+   * (N*H*D, H*D, D).  Otherwise each stride must be positive and a multiple
+   * of 8 elements (16 bytes). */
+  int64_t in_stride_b, in_stride_t, in_stride_h;
+  int64_t out_stride_b, out_stride_t, out_stride_h;
+  int32_t route;      /* SA_ROUTE_TAU or SA_ROUTE_TOPK */
+  float tau;          /* SA_ROUTE_TAU: any value but NaN; +inf keeps only the sink */
+  float topk_ratio;   /* SA_ROUTE_TOPK: in (0, 1] */
+  int32_t prefix_len; /* 0..N: rows of the packed prefix (sink + dense rows) */
+  float sm_scale;     /* softmax scale; <= 0 means 1/sqrt(D) */
+  uint32_t flags;     /* SA_FLAG_* bits; SA_FLAGS_DEFAULT is the method */
+} sparse_attn_params;
+
+typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
+
+/* Byte offsets of the workspace sections (all 256-byte aligned).  After
+ * sparse_attn_pool: qbar, kbar, vbar hold the fp32 block means
+ * [B, H, n_b, D]; kbar_bf16 and vbar_bf16 hold them rounded to bf16
+ * (round to nearest even) as [B, H, n_bp, D], n_bp = n_b rounded up to 64,
+ * padding rows zero.  After sparse_attn_select: counts [B, H, n_b] int32
+ * holds the number of selected key blocks per query block and lists
+ * [B, H, n_b, n_b] int32 holds them in ascending order in the first `count`
+ * entries of each row (the rest of the row is unspecified). */
+typedef struct sparse_attn_ws_layout {
+  uint64_t total_bytes;
+  uint64_t qbar, kbar, vbar;
+  uint64_t kbar_bf16, vbar_bf16;
+  uint64_t counts, lists;
+  int32_t n_blocks;        /* n_b */
+  int32_t n_blocks_padded; /* n_bp */
+  int32_t tail_rows;       /* valid rows of block n_b - 1 */
+  int32_t prefix_blocks;   /* ceil(prefix_len / 64), capped at n_b */
+  int32_t topk;            /* k of SA_ROUTE_TOPK, else 0 */
+  int32_t dense;           /* 1 if tau = -inf: every block exact, no routing */
+} sparse_attn_ws_layout;
+
+/* Validates *params (host only, touches no device) and creates a plan.
+ * Returns SA_EINVAL / SA_EUNSUPPORTED_SHAPE / SA_EALIGN on bad input, in
+ * which case *plan is set to NULL. */
+int sparse_attn_plan_create(const sparse_attn_params* params, sparse_attn_plan** plan);
+
+/* Frees a plan (NULL is ignored). */
+void sparse_attn_plan_destroy(sparse_attn_plan* plan);
+
+/* Fills *layout for the plan's shape (host only). */
+int sparse_attn_workspace_layout(const sparse_attn_plan* plan, sparse_attn_ws_layout* layout);
+
+/* Full forward: pool, select and attend (or attend alone on the dense path)
+ * enqueued on `stream` (a hipStream_t; NULL is the null stream).  q, k, v
+ * are read-only bf16 device pointers and may alias one another; out is a
+ * bf16 device pointer that must not overlap them.  ws points to at least
+ * layout.total_bytes of device memory (256-byte aligned), ws_bytes is its
+ * size; its contents on entry do not matter. */
+int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
+                        void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 1 alone: writes qbar, kbar, vbar, kbar_bf16 and vbar_bf16. */
+int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Steps 2-3 alone: scores every block pair from the pooled means already
+ * in ws and writes counts and lists (threshold or top-K, sink, dense
+ * prefix rows). */
+int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 4 alone: exact attention over each query block's list and centroid
+ * terms for every other block, from counts, lists and the bf16 centroids in
+ * ws.  A caller may write its own lists: entries must be distinct block
+ * indices in [0, n_b) (out-of-range entries are skipped), counts in
+ * [0, n_b]; a query block whose count is n_b gets no centroid term.  On the
+ * dense path the lists are not read. */
+int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
+                       void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Static message for an error code. */
+const char* sparse_attn_strerror(int code);
+
+/* Thread-local detail of the last failing call on this thread ("" if none),
+ * e.g. "requires gfx950, found gfx942". */
+const char* sparse_attn_last_error(void);
+
+/* SA_ABI_VERSION of the built library. */
+int sparse_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

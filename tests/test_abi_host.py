@@ -1,0 +1,172 @@
+"""Host-side checks of the C-ABI library (no GPU needed, nothing launched):
+the library loads, exports every function include/sparse_attn.h declares,
+validates parameters with the documented error codes and sizes the
+workspace as documented."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from block_sparse_video_fp32_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+SA_EINVAL, SA_EUNSUPPORTED_SHAPE, SA_EALIGN, SA_EWORKSPACE = -1, -2, -5, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(sparse_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("sparse_attn_plan_create", "sparse_attn_forward", "sparse_attn_pool",
+                 "sparse_attn_select", "sparse_attn_attend", "sparse_attn_workspace_layout"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.sparse_attn_abi_version() == 1
+
+
+def _params(**kw):
+    p = binding._Params()
+    p.B, p.N, p.H, p.D = 1, 1024, 2, 64
+    p.route, p.tau, p.prefix_len, p.flags = 0, 1.0, 0, 3
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _create(lib, p):
+    h = ctypes.c_void_p()
+    rc = lib.sparse_attn_plan_create(ctypes.byref(p), ctypes.byref(h))
+    if rc == 0:
+        lib.sparse_attn_plan_destroy(h)
+    else:
+        assert not h.value
+    return rc
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(), 0),
+        (dict(D=128), 0),
+        (dict(D=96), SA_EUNSUPPORTED_SHAPE),
+        (dict(D=256), SA_EUNSUPPORTED_SHAPE),
+        (dict(N=0), SA_EINVAL),
+        (dict(B=0), SA_EINVAL),
+        (dict(H=-1), SA_EINVAL),
+        (dict(N=131072), 0),
+        (dict(N=131073), SA_EUNSUPPORTED_SHAPE),
+        (dict(tau=float("nan")), SA_EINVAL),
+        (dict(tau=float("inf")), 0),
+        (dict(tau=float("-inf")), 0),
+        (dict(route=1, topk_ratio=0.0), SA_EINVAL),
+        (dict(route=1, topk_ratio=1.5), SA_EINVAL),
+        (dict(route=1, topk_ratio=float("nan")), SA_EINVAL),
+        (dict(route=1, topk_ratio=1.0), 0),
+        (dict(route=2), SA_EINVAL),
+        (dict(prefix_len=-1), SA_EINVAL),
+        (dict(prefix_len=1025), SA_EINVAL),
+        (dict(prefix_len=1024), 0),
+        (dict(sm_scale=float("inf")), SA_EINVAL),
+        (dict(flags=4), SA_EINVAL),
+        (dict(in_stride_b=3 * 1024 * 128, in_stride_t=3 * 128, in_stride_h=64), 0),
+        (dict(in_stride_b=1024 * 128, in_stride_t=130, in_stride_h=64), SA_EALIGN),
+        (dict(in_stride_b=0, in_stride_t=128, in_stride_h=64), SA_EINVAL),
+        (dict(out_stride_b=8, out_stride_t=-8, out_stride_h=8), SA_EINVAL),
+    ],
+)
+def test_plan_validation(lib, kw, code):
+    assert _create(lib, _params(**kw)) == code
+    if code:
+        assert lib.sparse_attn_last_error().decode() != ""
+        assert lib.sparse_attn_strerror(code).decode() not in ("", "unknown error")
+
+
+def test_null_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.sparse_attn_plan_create(None, ctypes.byref(h)) == SA_EINVAL
+    p = _params()
+    assert lib.sparse_attn_plan_create(ctypes.byref(p), None) == SA_EINVAL
+    lay = binding._Layout()
+    assert lib.sparse_attn_workspace_layout(None, ctypes.byref(lay)) == SA_EINVAL
+    lib.sparse_attn_plan_destroy(None)
+
+
+def test_workspace_layout_matches_documented_sizes():
+    plan = binding.SparseAttnPlan(2, 1000, 3, 128, tau=1.0, prefix_len=70)
+    L = plan.layout
+    nb = 16
+    assert L["n_blocks"] == nb and L["n_blocks_padded"] == 64
+    assert L["tail_rows"] == 1000 - 64 * 15 and L["prefix_blocks"] == 2 and L["dense"] == 0
+    offs = sorted((L[n], n) for n in ("qbar", "kbar", "vbar", "kbar_bf16", "vbar_bf16", "counts", "lists"))
+    sizes = dict(qbar=2 * 3 * nb * 128 * 4, kbar=2 * 3 * nb * 128 * 4, vbar=2 * 3 * nb * 128 * 4,
+                 kbar_bf16=2 * 3 * 64 * 128 * 2, vbar_bf16=2 * 3 * 64 * 128 * 2,
+                 counts=2 * 3 * nb * 4, lists=2 * 3 * nb * nb * 4)
+    for (o, n), (o2, _) in zip(offs, offs[1:] + [(L["total_bytes"], "end")]):
+        assert o % 256 == 0
+        assert o2 - o >= sizes[n]
+
+
+@pytest.mark.parametrize("ratio,nb,k", [(0.1, 598, 60), (0.1, 640, 64), (0.2, 512, 103), (1.0, 17, 17), (1e-9, 100, 1)])
+def test_topk_count(ratio, nb, k):
+    plan = binding.SparseAttnPlan(1, nb * 64, 1, 64, topk_ratio=ratio)
+    assert plan.layout["topk"] == k
+    from oracle import sol_oracle as O  # independent definition on the oracle side
+    assert O.topk_count(ratio, nb) == k
+
+
+def test_dense_flag():
+    assert binding.SparseAttnPlan(1, 128, 1, 64, tau=-math.inf).dense
+    assert not binding.SparseAttnPlan(1, 128, 1, 64, tau=math.inf).dense
+
+
+def test_call_validation_before_launch(lib):
+    """Errors that need no device: NULL tensors, misalignment, short workspace."""
+    plan = binding.SparseAttnPlan(1, 1024, 2, 64)
+    h = plan._h
+    need = plan.workspace_bytes
+    fake = 1 << 20  # never dereferenced: validation fails first
+    f = lib.sparse_attn_forward
+    assert f(h, None, fake, fake, fake, fake, need, None) == SA_EINVAL
+    assert f(h, fake + 2, fake, fake, fake, fake, need, None) == SA_EALIGN
+    assert f(h, fake, fake, fake, fake, fake + 16, need, None) == SA_EALIGN
+    assert f(h, fake, fake, fake, fake, fake, need - 1, None) == SA_EWORKSPACE
+    assert "plan needs" in lib.sparse_attn_last_error().decode()
+    assert f(None, fake, fake, fake, fake, fake, need, None) == SA_EINVAL
+    assert lib.sparse_attn_select(h, None, need, None) == SA_EINVAL
+    assert lib.sparse_attn_pool(h, fake, fake, fake, fake, need - 256, None) == SA_EWORKSPACE
+    assert lib.sparse_attn_attend(h, fake, fake, fake, None, fake, need, None) == SA_EINVAL
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+
+    plan = binding.SparseAttnPlan(1, 128, 1, 64)
+    x = torch.zeros(1, 128, 1, 64, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        plan.forward(x, x, x)
+    y = torch.zeros(1, 128, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        plan.forward(y, y, y)  # CPU tensors
+
+
+def test_plan_error_raises():
+    with pytest.raises(binding.SparseAttnError) as e:
+        binding.SparseAttnPlan(1, 128, 1, 96)
+    assert e.value.code == SA_EUNSUPPORTED_SHAPE and "64 or 128" in str(e.value)

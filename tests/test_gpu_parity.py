@@ -1,0 +1,322 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Bars:
+* pooled means: fp32 sums of 64 bf16 rows against the fp64 means, within
+  the fp32 summation bound (64 * 2^-24 * mean |x| per element, x2 slack);
+* selected-block lists: bit-exact against the oracle's routing, except
+  blocks within 1e-4 standard deviations of the row's threshold (or of the
+  k-th score in top-K mode), which must be under 0.1% of the routed blocks;
+* output, computed by the oracle on the GPU's own lists: max-abs <= 2e-2,
+  mean-abs <= 2e-3, cosine >= 0.9995 (bf16 output vs fp64).
+
+Small problems are compared on every output row; the large workloads
+(N = 16384 / 32768 / 38247, H = 56, D = 128) route every row and compare
+sampled query blocks (plus the tail and prefix blocks) one by one, in the
+launch configuration the benchmark times.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from block_sparse_video_fp32_amd import binding, inputs
+from oracle import sol_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS, MIN_COS = 2e-2, 2e-3, 0.9995
+BAND_SIGMA, BAND_MAX_FRAC = 1e-4, 1e-3
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _f32(bits):
+    return inputs.bf16_bits_to_f32(bits)
+
+
+class GpuRun:
+    """One forward through the C ABI; keeps the workspace for inspection."""
+
+    def __init__(self, q, k, v, strides=None, **kw):
+        dev = _dev()
+        B, N, H, D = q.shape
+        self.plan = binding.SparseAttnPlan(B, N, H, D, **kw)
+        self.q, self.k, self.v = (inputs.to_torch_bf16(x, dev) for x in (q, k, v))
+        self.out = torch.empty_like(self.q)
+        self.ws = self.plan.workspace(dev)
+        self.plan.forward(self.q, self.k, self.v, out=self.out, ws=self.ws)
+        torch.cuda.synchronize()
+        print(f"  gpu forward done: B={B} N={N} H={H} D={D} {kw}", flush=True)
+
+    def out_f64(self):
+        return self.out.float().cpu().numpy().astype(np.float64)
+
+    def selection(self):
+        counts, lists = self.plan.route_views(self.ws)
+        counts = counts.cpu().numpy()
+        lists = lists.cpu().numpy()
+        B, H, nb = counts.shape
+        assert ((counts >= 0) & (counts <= nb)).all()
+        valid = np.arange(nb)[None, None, None, :] < counts[..., None]
+        ent = np.where(valid, lists, -1)
+        assert ((ent[valid] >= 0) & (ent[valid] < nb)).all()
+        # ascending and distinct within each list
+        d = np.diff(np.where(valid, lists, np.iinfo(np.int32).max), axis=-1)
+        vv = valid[..., 1:]
+        assert (d[vv] > 0).all()
+        sel = np.zeros((B, H, nb, nb), dtype=bool)
+        bb, hh, aa, jj = np.nonzero(valid)
+        sel[bb, hh, aa, lists[bb, hh, aa, jj]] = True
+        return sel
+
+
+def check_route(sel_gpu, info, dense_rows_from=0):
+    """Lists equal the oracle's outside the 1e-4 sigma band; band < 0.1%."""
+    ref = info["sel"]
+    S, thr, sigma = info.get("S"), info["thr"], info["sigma"]
+    diff = sel_gpu != ref
+    if S is None:
+        assert not diff.any()
+        return 0.0
+    routed = ~np.isnan(thr) & np.isfinite(thr)
+    scale = np.abs(S).max(axis=-1)
+    band = np.abs(S - thr[..., None]) <= (BAND_SIGMA * sigma + 1e-6 * scale)[..., None]
+    band &= routed[..., None]
+    bad = diff & ~band
+    frac = band.sum() / max(1, routed.sum() * S.shape[-1])
+    assert not bad.any(), f"{int(bad.sum())} selection mismatches outside the band, first at {np.argwhere(bad)[:5]}"
+    assert frac < BAND_MAX_FRAC, f"band holds {frac:.2e} of routed blocks"
+    return frac
+
+
+def metrics(got, ref):
+    err = np.abs(got - ref)
+    cos = float((got * ref).sum() / math.sqrt((got * got).sum() * (ref * ref).sum()))
+    return float(err.max()), float(err.mean()), cos
+
+
+def check_output(got, ref, label=""):
+    mx, mean, cos = metrics(got, ref)
+    print(f"  {label} max-abs {mx:.3e} mean-abs {mean:.3e} cos {cos:.7f}", flush=True)
+    assert np.isfinite(got).all()
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and cos >= MIN_COS, (mx, mean, cos)
+
+
+def oracle_kw(kw):
+    return {k: kw[k] for k in ("tau", "topk_ratio", "prefix_len", "centroid", "logmass", "sm_scale") if k in kw}
+
+
+def full_parity(q, k, v, **kw):
+    run = GpuRun(q, k, v, **kw)
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    okw = oracle_kw(kw)
+    _, info = O.forward_blocks(qf, kf, vf, [], **okw)
+    dense = run.plan.dense
+    if not dense:
+        sel = run.selection()
+        check_route(sel, info)
+    else:
+        sel = info["sel"]
+    ref, _ = O.forward(qf, kf, vf, info=dict(info, sel=sel), **okw)
+    check_output(run.out_f64(), ref, f"N={q.shape[1]} {kw}")
+    return run, info
+
+
+# ----------------------------------------------------------------- pooling
+
+
+@pytest.mark.parametrize("N,D", [(1024, 64), (200, 128), (38247 - 37 * 1024, 128)])
+def test_pooled_means(N, D):
+    q, k, v = inputs.iid(2, N, 3, D, seed=N)
+    run = GpuRun(q, k, v, tau=1.0)
+    qb, kb, vb, kb16, vb16 = (t.float().cpu().numpy() for t in run.plan.pooled_views(run.ws))
+    for got, x in ((qb, q), (kb, k), (vb, v)):
+        xf = _f32(x).astype(np.float64)
+        ref = O.pool(xf)
+        bound = 2 * 64 * 2.0**-24 * np.abs(xf).max()
+        assert np.abs(got - ref).max() <= bound
+    nb = qb.shape[2]
+    # bf16 copies are the fp32 means rounded to nearest even; padding rows are zero
+    for got16, f in ((kb16, kb), (vb16, vb)):
+        want = _f32(inputs.f32_to_bf16_bits(f))
+        np.testing.assert_array_equal(got16[:, :, :nb], want)
+        assert (got16[:, :, nb:] == 0).all()
+
+
+# ---------------------------------------------------- small, every output row
+
+
+SMALL = [
+    ("tiny_tau1", dict(kind="tiny"), dict(tau=1.0)),
+    ("tail_d64", dict(B=2, N=200, H=3, D=64), dict(tau=1.0)),
+    ("tail_d128", dict(B=1, N=1000, H=2, D=128), dict(tau=1.0)),
+    ("tau0", dict(B=1, N=1024, H=2, D=128), dict(tau=0.0)),
+    ("tau_inf_sink", dict(B=1, N=700, H=2, D=64), dict(tau=math.inf, prefix_len=130)),
+    ("topk", dict(B=1, N=1500, H=2, D=128), dict(topk_ratio=0.25)),
+    ("topk_prefix", dict(B=2, N=1100, H=2, D=64), dict(topk_ratio=0.1, prefix_len=100)),
+    ("prefix_tau", dict(B=1, N=1024, H=3, D=128), dict(tau=1.0, prefix_len=64)),
+    ("no_centroid", dict(B=1, N=1024, H=2, D=128), dict(tau=1.0, centroid=False)),
+    ("no_logmass", dict(B=1, N=1024, H=2, D=64), dict(tau=1.0, logmass=False)),
+    ("scale", dict(B=1, N=512, H=2, D=64), dict(tau=0.5, sm_scale=0.3)),
+    ("dense_tail", dict(B=1, N=777, H=2, D=128), dict(tau=-math.inf)),
+    ("dense_d64", dict(B=2, N=256, H=1, D=64), dict(tau=-math.inf)),
+    ("one_row", dict(B=1, N=1, H=1, D=64), dict(tau=1.0)),
+    ("one_block", dict(B=1, N=64, H=2, D=128), dict(tau=1.0)),
+]
+
+
+def _small_inputs(shape, seed):
+    if shape.get("kind") == "tiny":
+        w = inputs.make_workload("tiny")
+        return w.q, w.k, w.v
+    B, N, H, D = shape["B"], shape["N"], shape["H"], shape["D"]
+    if N >= 256:
+        return inputs.clustered(B, N, H, D, seed)
+    return inputs.iid(B, N, H, D, seed)
+
+
+@pytest.mark.parametrize("name,shape,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_full_parity(name, shape, kw):
+    q, k, v = _small_inputs(shape, seed=len(name))
+    full_parity(q, k, v, **kw)
+
+
+def test_tiny_matches_oracle_lists_exactly():
+    w = inputs.make_workload("tiny")
+    run = GpuRun(w.q, w.k, w.v, tau=1.0)
+    _, info = O.forward_blocks(_f32(w.q), _f32(w.k), _f32(w.v), [], tau=1.0)
+    np.testing.assert_array_equal(run.selection(), info["sel"])
+
+
+def test_deterministic_reruns():
+    q, k, v = inputs.clustered(1, 2048, 4, 128, seed=5)
+    a = GpuRun(q, k, v, tau=1.0)
+    o1 = a.out.clone()
+    a.plan.forward(a.q, a.k, a.v, out=a.out, ws=a.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), a.out.view(torch.int16))
+
+
+def test_strided_fused_qkv_views():
+    """q, k, v as strided views of one [B, N, 3, H, D] projection output."""
+    dev = _dev()
+    B, N, H, D = 1, 1100, 2, 128
+    q, k, v = inputs.clustered(B, N, H, D, seed=9)
+    fused = np.stack([q, k, v], axis=2)  # [B, N, 3, H, D]
+    ft = inputs.to_torch_bf16(fused, dev)
+    tq, tk, tv = ft[:, :, 0], ft[:, :, 1], ft[:, :, 2]
+    out = binding.sparse_attn(tq, tk, tv, tau=1.0)
+    torch.cuda.synchronize()
+    ref_run = GpuRun(q, k, v, tau=1.0)
+    assert torch.equal(out.view(torch.int16), ref_run.out.view(torch.int16))
+
+
+def test_injected_lists_through_attend():
+    """sparse_attn_attend on caller-written lists (random masks, including
+    empty lists) against the oracle on the same mask."""
+    dev = _dev()
+    B, N, H, D = 1, 1000, 2, 128
+    q, k, v = inputs.clustered(B, N, H, D, seed=3)
+    plan = binding.SparseAttnPlan(B, N, H, D, tau=1.0)
+    tq, tk, tv = (inputs.to_torch_bf16(x, dev) for x in (q, k, v))
+    ws = plan.workspace(dev)
+    plan.pool(tq, tk, tv, ws)
+    nb = plan.layout["n_blocks"]
+    rng = np.random.default_rng(0)
+    sel = rng.random((B, H, nb, nb)) < 0.2
+    sel[0, 0, 3] = False  # a query block with nothing exact
+    sel[0, 1, 5] = True   # a fully exact query block
+    counts, lists = plan.route_views(ws)
+    cnt = sel.sum(-1).astype(np.int32)
+    lst = np.zeros((B, H, nb, nb), dtype=np.int32)
+    for h in range(H):
+        for a in range(nb):
+            idx = np.nonzero(sel[0, h, a])[0]
+            lst[0, h, a, : len(idx)] = idx[::-1] if a % 2 else idx  # order must not matter
+    counts.copy_(torch.from_numpy(cnt))
+    lists.copy_(torch.from_numpy(lst))
+    out = torch.empty_like(tq)
+    plan.attend(tq, tk, tv, out, ws)
+    torch.cuda.synchronize()
+    ref, _ = O.forward(_f32(q), _f32(k), _f32(v), mask=sel)
+    check_output(out.float().cpu().numpy().astype(np.float64), ref, "injected")
+
+
+def test_max_blocks():
+    """n_b = 2048 (N = 131072), the largest supported length."""
+    B, N, H, D = 1, 131072, 1, 64
+    q, k, v = inputs.clustered(B, N, H, D, seed=12)
+    run = GpuRun(q, k, v, tau=1.0)
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    _, info = O.forward_blocks(qf, kf, vf, [], tau=1.0)
+    sel = run.selection()
+    check_route(sel, info)
+    blocks = [(0, 0, a) for a in (0, 1, 777, 1500, 2047)]
+    parts, _ = O.forward_blocks(qf, kf, vf, blocks, info=dict(info, sel=sel))
+    got = run.out_f64()
+    for (b, h, a), ref in parts.items():
+        check_output(got[b, a * 64 : a * 64 + ref.shape[0], h], ref, f"block {a}")
+
+
+# -------------------------------------------- the benchmarked workloads
+
+
+def _sampled_parity(name, n_sample=48, **over):
+    w = inputs.make_workload(name, **over)
+    kw = dict(tau=w.tau, topk_ratio=w.topk_ratio, prefix_len=w.prefix_len)
+    if w.topk_ratio is not None:
+        kw.pop("tau")
+    else:
+        kw.pop("topk_ratio")
+    print(f"  {name}: generated {w.shape}", flush=True)
+    run = GpuRun(w.q, w.k, w.v, **kw)
+    qf, kf, vf = _f32(w.q), (None if w.k is w.q else _f32(w.k)), _f32(w.v)
+    kf = qf if kf is None else kf
+    _, info = O.forward_blocks(qf, kf, vf, [], **oracle_kw(kw))
+    B, N, H, D = w.shape
+    nb = O.num_blocks(N)
+    if run.plan.dense:
+        sel = info["sel"]
+    else:
+        sel = run.selection()
+        frac = check_route(sel, info)
+        print(f"  {name}: density {sel.mean():.4f} oracle {info['sel'].mean():.4f} band {frac:.2e}", flush=True)
+    rng = np.random.default_rng(1)
+    blocks = {(0, int(rng.integers(H)), int(rng.integers(nb))) for _ in range(n_sample)}
+    blocks |= {(0, 0, nb - 1), (0, H - 1, nb - 1), (0, 3, 0)}
+    pb = O.prefix_blocks(w.prefix_len)
+    if pb:
+        blocks |= {(0, 5, pb - 1), (0, 6, pb)}
+    parts, _ = O.forward_blocks(qf, kf, vf, sorted(blocks), info=dict(info, sel=sel), **oracle_kw(kw))
+    got = run.out_f64()
+    g = np.concatenate([got[b, a * 64 : a * 64 + r.shape[0], h] for (b, h, a), r in parts.items()])
+    r = np.concatenate(list(parts.values()))
+    check_output(g, r, f"{name} ({len(parts)} blocks)")
+
+
+def test_workload_n4k_full():
+    w = inputs.make_workload("n4k")
+    full_parity(w.q, w.k, w.v, tau=1.0)
+
+
+def test_workload_n16k_sampled():
+    _sampled_parity("n16k")
+
+
+def test_workload_n16k_dense_sampled():
+    _sampled_parity("n16k", tau=-math.inf)
+
+
+def test_workload_n32k_sampled():
+    _sampled_parity("n32k")
+
+
+def test_workload_h3_sampled():
+    _sampled_parity("h3")
