@@ -136,8 +136,10 @@ def route(
     """Block selection from the score matrix S [B, H, n_b, n_b].
 
     Returns a dict with ``sel`` (bool [B, H, n_b, n_b]) and, per row, ``mu``,
-    ``sigma`` and ``thr`` (the tau threshold, or the k-th largest score in
-    top-K mode; NaN where the row is dense).
+    ``sigma``, ``thr`` (the tau threshold, or the k-th largest score in
+    top-K mode) and ``cut``, the score value that separates kept from dropped
+    blocks (thr in tau mode; in top-K mode the midpoint between the k-th and
+    (k+1)-th largest scores, -inf when k = n_b).  Both are NaN on dense rows.
     """
     B, H, nb, nb2 = S.shape
     assert nb == nb2
@@ -152,6 +154,11 @@ def route(
         sel = np.zeros(S.shape, dtype=bool)
         np.put_along_axis(sel, order[..., :k], True, axis=-1)
         thr = np.take_along_axis(S, order[..., k - 1 : k], axis=-1)[..., 0]
+        if k < nb:
+            nxt = np.take_along_axis(S, order[..., k : k + 1], axis=-1)[..., 0]
+            cut = 0.5 * (thr + nxt)
+        else:
+            cut = np.full(mu.shape, -math.inf)
     else:
         t = float(np.float32(tau))
         if t == -math.inf:
@@ -162,13 +169,15 @@ def route(
         else:
             thr = mu + t * sigma
             sel = S >= thr[..., None]
+        cut = thr.copy()
     # Exact KV sink: every key block that holds a prefix row.
     sel[..., :pb] = True
     # Prefix query rows see every key exactly.
     sel[:, :, :pb, :] = True
     if pb:
         thr[:, :, :pb] = np.nan
-    return dict(sel=sel, mu=mu, sigma=sigma, thr=thr)
+        cut[:, :, :pb] = np.nan
+    return dict(sel=sel, mu=mu, sigma=sigma, thr=thr, cut=cut)
 
 
 def selection_lists(sel: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:

@@ -4,8 +4,9 @@ Bars:
 * pooled means: fp32 sums of 64 bf16 rows against the fp64 means, within
   the fp32 summation bound (64 * 2^-24 * mean |x| per element, x2 slack);
 * selected-block lists: bit-exact against the oracle's routing, except
-  blocks within 1e-4 standard deviations of the row's threshold (or of the
-  k-th score in top-K mode), which must be under 0.1% of the routed blocks;
+  blocks within 1e-4 standard deviations of the row's cut (the tau
+  threshold, or in top-K mode the midpoint between the k-th and (k+1)-th
+  scores), which must be under 0.1% of the routed blocks;
 * output, computed by the oracle on the GPU's own lists: max-abs <= 2e-2,
   mean-abs <= 2e-3, cosine >= 0.9995 (bf16 output vs fp64).
 
@@ -80,7 +81,7 @@ class GpuRun:
 def check_route(sel_gpu, info, dense_rows_from=0):
     """Lists equal the oracle's outside the 1e-4 sigma band; band < 0.1%."""
     ref = info["sel"]
-    S, thr, sigma = info.get("S"), info["thr"], info["sigma"]
+    S, thr, sigma = info.get("S"), info["cut"], info["sigma"]
     diff = sel_gpu != ref
     if S is None:
         assert not diff.any()
@@ -90,9 +91,13 @@ def check_route(sel_gpu, info, dense_rows_from=0):
     band = np.abs(S - thr[..., None]) <= (BAND_SIGMA * sigma + 1e-6 * scale)[..., None]
     band &= routed[..., None]
     bad = diff & ~band
-    frac = band.sum() / max(1, routed.sum() * S.shape[-1])
+    n_routed = int(routed.sum()) * S.shape[-1]
+    frac = band.sum() / max(1, n_routed)
     assert not bad.any(), f"{int(bad.sum())} selection mismatches outside the band, first at {np.argwhere(bad)[:5]}"
-    assert frac < BAND_MAX_FRAC, f"band holds {frac:.2e} of routed blocks"
+    # The share bar needs at least 1000 routed blocks: below that, 0.1% is
+    # less than one block (a lone block always sits at its own row's cut).
+    if n_routed >= 1000:
+        assert frac < BAND_MAX_FRAC, f"band holds {frac:.2e} of routed blocks"
     return frac
 
 
