@@ -166,7 +166,7 @@ def main():
     def step():
         plan.pool(q, k, v, ws)
         plan.select(ws)
-        plan.attend(q, k, v, out, ws)
+        plan.attend(q, out, ws)
 
     for _ in range(args.warmup):
         step()
@@ -184,7 +184,7 @@ def main():
         ev[i][1].record(stream)
         plan.select(ws)
         ev[i][2].record(stream)
-        plan.attend(q, k, v, out, ws)
+        plan.attend(q, out, ws)
         ev[i][3].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
@@ -219,7 +219,11 @@ def main():
         print(f"# dense: {dense_ms:.3f} ms/call", file=sys.stderr, flush=True)
 
     dense_flops = 4.0 * B * H * N * N * D
-    pool_bytes = 3 * B * N * H * D * 2 + 3 * B * H * nb * D * 4 + 2 * B * H * plan.layout["n_blocks_padded"] * D * 2
+    # pool = pool_q (reads Q, writes Qbar) + pack_kv (reads K, V; writes Kbar,
+    # Vbar, the packed K and V^T tiles and the packed bf16 centroids)
+    nbp = plan.layout["n_blocks_padded"]
+    pool_bytes = (3 * B * N * H * D * 2 + 3 * B * H * nb * D * 4
+                  + 2 * B * H * nb * 64 * D * 2 + 2 * B * H * nbp * D * 2)
     sel_bytes = 2 * B * H * nb * D * 4 + B * H * nb * 4 + density * B * H * nb * nb * 4
     achieved = flops / (t_att * 1e-3) / 1e12
     traffic = _traffic(args.workload)

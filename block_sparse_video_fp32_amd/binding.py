@@ -72,8 +72,10 @@ class _Layout(ctypes.Structure):
         ("qbar", ctypes.c_uint64),
         ("kbar", ctypes.c_uint64),
         ("vbar", ctypes.c_uint64),
-        ("kbar_bf16", ctypes.c_uint64),
-        ("vbar_bf16", ctypes.c_uint64),
+        ("k_packed", ctypes.c_uint64),
+        ("v_packed", ctypes.c_uint64),
+        ("kbar_packed", ctypes.c_uint64),
+        ("vbar_packed", ctypes.c_uint64),
         ("counts", ctypes.c_uint64),
         ("lists", ctypes.c_uint64),
         ("n_blocks", ctypes.c_int32),
@@ -120,7 +122,7 @@ def load_library() -> ctypes.CDLL:
         lib.sparse_attn_pool.restype = i32
         lib.sparse_attn_select.argtypes = [vp, vp, sz, vp]
         lib.sparse_attn_select.restype = i32
-        lib.sparse_attn_attend.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.sparse_attn_attend.argtypes = [vp, vp, vp, vp, sz, vp]
         lib.sparse_attn_attend.restype = i32
         lib.sparse_attn_strerror.argtypes = [i32]
         lib.sparse_attn_strerror.restype = ctypes.c_char_p
@@ -273,10 +275,11 @@ class SparseAttnPlan:
         self._call(self._lib.sparse_attn_select, "sparse_attn_select", ws.device, _ptr(ws), ws.numel())
         return ws
 
-    def attend(self, q, k, v, out, ws):
-        self._check_io(q, k, v, out)
+    def attend(self, q, out, ws):
+        """Step 4 alone; reads the packed tiles and lists already in ws."""
+        self._check_io(q, out)
         self._call(self._lib.sparse_attn_attend, "sparse_attn_attend", q.device,
-                   _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws), ws.numel())
+                   _ptr(q), _ptr(out), _ptr(ws), ws.numel())
         return out
 
     # -- workspace views -----------------------------------------------------
@@ -300,14 +303,25 @@ class SparseAttnPlan:
         return counts, lists
 
     def pooled_views(self, ws):
-        """fp32 (qbar, kbar, vbar) [B,H,n_b,D] and bf16 (kbar16, vbar16) [B,H,n_bp,D]."""
+        """fp32 block means (qbar, kbar, vbar), each [B, H, n_b, D]."""
+        import torch
+
+        B, N, H, D = self.shape
+        nb = self.layout["n_blocks"]
+        return tuple(self._view(ws, n, torch.float32, (B, H, nb, D)) for n in ("qbar", "kbar", "vbar"))
+
+    def packed_views(self, ws):
+        """bf16 packed tiles: k_packed, v_packed [B, H, n_b, 2, 32*D] and
+        kbar_packed, vbar_packed [B, H, n_bp/32, 32*D] (orders in sparse_attn.h)."""
         import torch
 
         B, N, H, D = self.shape
         nb, nbp = self.layout["n_blocks"], self.layout["n_blocks_padded"]
-        f = [self._view(ws, n, torch.float32, (B, H, nb, D)) for n in ("qbar", "kbar", "vbar")]
-        b = [self._view(ws, n, torch.bfloat16, (B, H, nbp, D)) for n in ("kbar_bf16", "vbar_bf16")]
-        return (*f, *b)
+        kp = self._view(ws, "k_packed", torch.bfloat16, (B, H, nb, 2, 32 * D))
+        vp = self._view(ws, "v_packed", torch.bfloat16, (B, H, nb, 2, 32 * D))
+        kbp = self._view(ws, "kbar_packed", torch.bfloat16, (B, H, nbp // 32, 32 * D))
+        vbp = self._view(ws, "vbar_packed", torch.bfloat16, (B, H, nbp // 32, 32 * D))
+        return kp, vp, kbp, vbp
 
 
 def sparse_attn(

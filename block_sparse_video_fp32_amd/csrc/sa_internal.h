@@ -28,20 +28,24 @@ struct Shape {
   int centroid;             // centroid terms on
 };
 
+// Device workspace sections (see the layout notes in sparse_attn.h).
 struct Workspace {
-  float* qbar;
+  float* qbar;    // [B,H,nb,D] fp32 block means
   float* kbar;
   float* vbar;
-  uint16_t* kbar16;
-  uint16_t* vbar16;
+  uint16_t* kp;   // K of every block in MFMA fragment order, bf16
+  uint16_t* vp;   // V^T of every block in MFMA fragment order, bf16
+  uint16_t* kbp;  // centroids Kbar in the same packed order, bf16
+  uint16_t* vbp;  // centroids Vbar^T in the same packed order, bf16
   int* counts;
   int* lists;
 };
 
-hipError_t launch_pool(const Shape& s, const void* q, const void* k, const void* v,
-                       const Workspace& ws, hipStream_t stream);
+hipError_t launch_pool_q(const Shape& s, const void* q, const Workspace& ws, hipStream_t stream);
+hipError_t launch_pack_kv(const Shape& s, const void* k, const void* v, const Workspace& ws,
+                          hipStream_t stream);
 hipError_t launch_select(const Shape& s, const Workspace& ws, hipStream_t stream);
-hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v, void* out,
-                         const Workspace& ws, hipStream_t stream);
+hipError_t launch_attend(const Shape& s, const void* q, void* out, const Workspace& ws,
+                         hipStream_t stream);
 
 }  // namespace sa

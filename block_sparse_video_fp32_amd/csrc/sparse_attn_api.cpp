@@ -158,13 +158,16 @@ void build_plan(sparse_attn_plan* pl) {
   std::memset(&L, 0, sizeof(L));
   const uint64_t bh = (uint64_t)p.B * p.H;
   const uint64_t pooled = bh * s.nb * p.D * sizeof(float);
-  const uint64_t pooled16 = bh * s.nbp * p.D * sizeof(uint16_t);
+  const uint64_t packed = bh * s.nb * 64ull * p.D * sizeof(uint16_t);
+  const uint64_t cpacked = bh * s.nbp * (uint64_t)p.D * sizeof(uint16_t);
   uint64_t off = 0;
   L.qbar = off; off = align256(off + pooled);
   L.kbar = off; off = align256(off + pooled);
   L.vbar = off; off = align256(off + pooled);
-  L.kbar_bf16 = off; off = align256(off + pooled16);
-  L.vbar_bf16 = off; off = align256(off + pooled16);
+  L.k_packed = off; off = align256(off + packed);
+  L.v_packed = off; off = align256(off + packed);
+  L.kbar_packed = off; off = align256(off + cpacked);
+  L.vbar_packed = off; off = align256(off + cpacked);
   L.counts = off; off = align256(off + bh * s.nb * sizeof(int32_t));
   L.lists = off; off = align256(off + bh * s.nb * (uint64_t)s.nb * sizeof(int32_t));
   L.total_bytes = off;
@@ -183,8 +186,10 @@ sa::Workspace carve(const sparse_attn_plan* pl, void* ws) {
   w.qbar = reinterpret_cast<float*>(base + L.qbar);
   w.kbar = reinterpret_cast<float*>(base + L.kbar);
   w.vbar = reinterpret_cast<float*>(base + L.vbar);
-  w.kbar16 = reinterpret_cast<uint16_t*>(base + L.kbar_bf16);
-  w.vbar16 = reinterpret_cast<uint16_t*>(base + L.vbar_bf16);
+  w.kp = reinterpret_cast<uint16_t*>(base + L.k_packed);
+  w.vp = reinterpret_cast<uint16_t*>(base + L.v_packed);
+  w.kbp = reinterpret_cast<uint16_t*>(base + L.kbar_packed);
+  w.vbp = reinterpret_cast<uint16_t*>(base + L.vbar_packed);
   w.counts = reinterpret_cast<int*>(base + L.counts);
   w.lists = reinterpret_cast<int*>(base + L.lists);
   return w;
@@ -262,8 +267,10 @@ int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k,
   if ((rc = check_tensors(q, k, v, nullptr, false))) return rc;
   if ((rc = check_ws(plan, ws, ws_bytes))) return rc;
   if ((rc = check_device())) return rc;
-  if ((rc = launched(sa::launch_pool(plan->shape, q, k, v, carve(plan, ws), (hipStream_t)stream), "pool")))
-    return rc;
+  const sa::Workspace w = carve(plan, ws);
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = launched(sa::launch_pool_q(plan->shape, q, w, st), "pool_q"))) return rc;
+  if ((rc = launched(sa::launch_pack_kv(plan->shape, k, v, w, st), "pack_kv"))) return rc;
   return ok();
 }
 
@@ -277,15 +284,14 @@ int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, 
   return ok();
 }
 
-int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
-                       void* out, void* ws, size_t ws_bytes, void* stream) {
+int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, void* out, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (!plan) return fail(SA_EINVAL, "plan is NULL");
   int rc;
-  if ((rc = check_tensors(q, k, v, out, true))) return rc;
+  if ((rc = check_tensors(q, q, q, out, true))) return rc;
   if ((rc = check_ws(plan, ws, ws_bytes))) return rc;
   if ((rc = check_device())) return rc;
-  if ((rc = launched(sa::launch_attend(plan->shape, q, k, v, out, carve(plan, ws), (hipStream_t)stream),
-                     "attend")))
+  if ((rc = launched(sa::launch_attend(plan->shape, q, out, carve(plan, ws), (hipStream_t)stream), "attend")))
     return rc;
   return ok();
 }
@@ -300,10 +306,13 @@ int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void*
   const sa::Workspace w = carve(plan, ws);
   hipStream_t st = (hipStream_t)stream;
   if (!plan->shape.dense) {
-    if ((rc = launched(sa::launch_pool(plan->shape, q, k, v, w, st), "pool"))) return rc;
+    if ((rc = launched(sa::launch_pool_q(plan->shape, q, w, st), "pool_q"))) return rc;
+  }
+  if ((rc = launched(sa::launch_pack_kv(plan->shape, k, v, w, st), "pack_kv"))) return rc;
+  if (!plan->shape.dense) {
     if ((rc = launched(sa::launch_select(plan->shape, w, st), "select"))) return rc;
   }
-  if ((rc = launched(sa::launch_attend(plan->shape, q, k, v, out, w, st), "attend"))) return rc;
+  if ((rc = launched(sa::launch_attend(plan->shape, q, out, w, st), "attend"))) return rc;
   return ok();
 }
 

@@ -1,9 +1,12 @@
 // gfx950 kernels of routed block-sparse attention.
 //
-//   pool_kernel    per-64-row-block means of Q, K, V in FP32 (HBM-bound
-//                  stream), plus bf16 copies of the K and V centroids for the
-//                  MFMA centroid pass (Star7 README, 工作原理 > Sol: Q64/K64
-//                  blocks; Spark-H3 news, Spark-Reweight: mean-pooled K/V).
+//   pool_q_kernel  per-64-row-block means of Q in FP32 (HBM-bound stream;
+//                  Star7 README, 工作原理 > Sol: Q64/K64 blocks).
+//   pack_kv_kernel per block of one head: the FP32 means of K and V (the
+//                  centroids; Spark-H3 news, Spark-Reweight: mean-pooled K/V
+//                  summaries), plus K, V^T and the centroids rewritten in the
+//                  register order of the attend kernel's MFMA operands, so
+//                  that every operand load there is one coalesced 1 KB read.
 //   select_kernel  fp32 block scores Qbar_a . Kbar_c for a group of query
 //                  blocks against every key block, then per query block
 //                  (one wave each) the threshold mean + tau * std (two-pass,
@@ -11,12 +14,22 @@
 //                  ballot compaction into an ascending index list
 //                  (thakicloud accel-stack post, 이 기술은 무엇인가; Spark-H3
 //                  news, 워크플로: topk_ratio).
-//   attend_kernel  one workgroup per (b, h, query block): exact bf16
-//                  attention on MFMA over the listed key blocks, then one
-//                  centroid logit per unselected block with the log-mass bias,
-//                  all merged into the same FP32 online softmax (Star7 README,
-//                  Sol: missed blocks contribute through a K/V centroid in the
+//   attend_kernel  one wave per (b, h, query block): exact bf16 attention on
+//                  MFMA over the listed key blocks, then one centroid logit
+//                  per unselected block with the log-mass bias, all merged
+//                  into the same FP32 online softmax (Star7 README, Sol:
+//                  missed blocks contribute through a K/V centroid in the
 //                  same FP32 online softmax).
+//
+// Packed operand layouts (bf16).  A "half tile" is 32 keys x D.
+//   K half tile:   element ((kt*NS + ss)*64 + lane)*8 + e holds
+//                  K[16 kt + lane%16][32 ss + 8 (lane/16) + e]   (NS = D/32)
+//   V^T half tile: element d*32 + 8 g + e holds V[keyslot(g, e)][d] with
+//                  keyslot(g, e) = 4 g + e for e < 4, 16 + 4 g + e - 4 else.
+// These are the A-operand registers of v_mfma_f32_16x16x32_bf16 for
+// S^T = K Q^T and O^T = V^T P^T; keyslot() is the order in which the S^T
+// accumulator holds the keys, so P^T goes from accumulator to B operand
+// without any lane movement.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -46,11 +59,6 @@ __device__ __forceinline__ float lane_bf16(const uint4& w, int e) {
   return bf16_bits_to_f32((e & 1) ? (word >> 16) : (word & 0xffffu));
 }
 
-__device__ __forceinline__ uint32_t half16(const uint4& w, int e) {
-  const uint32_t word = (e < 2) ? w.x : (e < 4) ? w.y : (e < 6) ? w.z : w.w;
-  return (e & 1) ? (word >> 16) : (word & 0xffffu);
-}
-
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
@@ -63,14 +71,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ---------------------------------------------------------------------------
-// pool: grid (n_bp, 3 tensors, B * head groups), 256 threads.  A thread owns
-// one 16-byte column chunk (8 values of one head) and sums half of the
-// block's rows; the two halves are added in a fixed order.
+// pool_q: grid (n_b, 1, B * head groups), 256 threads.  A thread owns one
+// 16-byte column chunk (8 values of one head) and sums half of the block's
+// rows; the two halves are added in a fixed order.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void pool_kernel(Shape s, const uint16_t* __restrict__ q,
-                                                   const uint16_t* __restrict__ k,
-                                                   const uint16_t* __restrict__ v, Workspace ws) {
+__global__ __launch_bounds__(256) void pool_q_kernel(Shape s, const uint16_t* __restrict__ q, Workspace ws) {
   constexpr int CPH = D / 8;          // chunks per head row
   constexpr int HG = 128 / CPH;       // heads per workgroup
   constexpr int CHUNKS = HG * CPH;    // 128 chunks
@@ -79,7 +85,6 @@ __global__ __launch_bounds__(256) void pool_kernel(Shape s, const uint16_t* __re
   __shared__ float part[CHUNKS * 8];
 
   const int j = blockIdx.x;
-  const int t = blockIdx.y;
   const int hgroups = (s.H + HG - 1) / HG;
   const int b = blockIdx.z / hgroups;
   const int hg = blockIdx.z - b * hgroups;
@@ -91,22 +96,13 @@ __global__ __launch_bounds__(256) void pool_kernel(Shape s, const uint16_t* __re
   const bool active = h < s.H;
   const long long bh = (long long)b * s.H + h;
 
-  if (j >= s.nb) {  // zero padding rows of the bf16 centroid arrays
-    if (t > 0 && active && half == 0) {
-      uint16_t* dst = (t == 1 ? ws.kbar16 : ws.vbar16) + (bh * s.nbp + j) * D + d0;
-      *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
-    }
-    return;
-  }
-
-  const uint16_t* src = (t == 0) ? q : (t == 1) ? k : v;
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   const int r0 = j * kBlock + half * RPS;
   const int rend = min(s.N, r0 + RPS);
   if (active && r0 < rend) {
-    const uint16_t* p = src + (long long)b * s.isb + (long long)h * s.ish + d0 + (long long)r0 * s.ist;
+    const uint16_t* p = q + (long long)b * s.isb + (long long)h * s.ish + d0 + (long long)r0 * s.ist;
     const int n = rend - r0;
     int r = 0;
     for (; r + 8 <= n; r += 8) {
@@ -134,17 +130,111 @@ __global__ __launch_bounds__(256) void pool_kernel(Shape s, const uint16_t* __re
     float m[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) m[e] = (acc[e] + part[chunk * 8 + e]) / n;
-    float* dst = (t == 0 ? ws.qbar : t == 1 ? ws.kbar : ws.vbar) + (bh * s.nb + j) * D + d0;
+    float* dst = ws.qbar + (bh * s.nb + j) * D + d0;
     reinterpret_cast<float4*>(dst)[0] = make_float4(m[0], m[1], m[2], m[3]);
     reinterpret_cast<float4*>(dst)[1] = make_float4(m[4], m[5], m[6], m[7]);
-    if (t > 0) {
-      uint4 w;
-      w.x = f32_to_bf16_bits(m[0]) | (f32_to_bf16_bits(m[1]) << 16);
-      w.y = f32_to_bf16_bits(m[2]) | (f32_to_bf16_bits(m[3]) << 16);
-      w.z = f32_to_bf16_bits(m[4]) | (f32_to_bf16_bits(m[5]) << 16);
-      w.w = f32_to_bf16_bits(m[6]) | (f32_to_bf16_bits(m[7]) << 16);
-      uint16_t* d16 = (t == 1 ? ws.kbar16 : ws.vbar16) + (bh * s.nbp + j) * D + d0;
-      *reinterpret_cast<uint4*>(d16) = w;
+  }
+}
+
+// Position of key r (0..31 within a half tile) in the packed V^T order.
+__device__ __forceinline__ int v_slot(int r) {
+  return (r & 16) ? 8 * ((r - 16) >> 2) + 4 + (r & 3) : 8 * (r >> 2) + (r & 3);
+}
+// Key held in packed V^T position 8 g + e.
+__device__ __forceinline__ int v_key(int g, int e) { return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4); }
+
+// ---------------------------------------------------------------------------
+// pack_kv: grid (n_bp, H, B), 256 threads.  Stages the block's K and V rows
+// (zero past N) in LDS, writes the fp32 means Kbar, Vbar (sequential row
+// sums), the packed half tiles of K and V^T, and the bf16 centroids into
+// their packed centroid half tile (block j is centroid row j % 32 of centroid
+// half tile j / 32).  Blocks j >= n_b only zero their centroid rows.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* __restrict__ k,
+                                                      const uint16_t* __restrict__ v, Workspace ws) {
+  constexpr int NS = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int LS = D + 8;  // LDS row stride (bf16)
+  constexpr int HT = 32 * D; // elements of one packed half tile
+  __shared__ __attribute__((aligned(16))) uint16_t Kl[64 * LS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vl[64 * LS];
+
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const long long bh = (long long)b * s.H + h;
+  const int tid = threadIdx.x;
+  const int J = j >> 5, r = j & 31;  // centroid half tile and row
+  uint16_t* kc = ws.kbp + (bh * (s.nbp / 32) + J) * HT;
+  uint16_t* vc = ws.vbp + (bh * (s.nbp / 32) + J) * HT;
+  const int ckt = r >> 4, cl16 = r & 15;
+  auto kc_index = [&](int d) {
+    const int ss = d >> 5, g = (d & 31) >> 3, e = d & 7;
+    return ((ckt * NS + ss) * 64 + 16 * g + cl16) * 8 + e;
+  };
+
+  if (j >= s.nb) {
+    if (tid < D) {
+      kc[kc_index(tid)] = 0;
+      vc[tid * 32 + v_slot(r)] = 0;
+    }
+    return;
+  }
+
+  const int n = min(kBlock, s.N - j * kBlock);
+  const long long base = (long long)b * s.isb + (long long)h * s.ish + (long long)j * kBlock * s.ist;
+#pragma unroll
+  for (int i = 0; i < CPR / 4; ++i) {
+    const int id = tid + 256 * i;
+    const int row = id / CPR, col = id % CPR;
+    uint4 xk = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
+    if (row < n) {
+      xk = *reinterpret_cast<const uint4*>(k + base + (long long)row * s.ist + col * 8);
+      xv = *reinterpret_cast<const uint4*>(v + base + (long long)row * s.ist + col * 8);
+    }
+    *reinterpret_cast<uint4*>(Kl + row * LS + col * 8) = xk;
+    *reinterpret_cast<uint4*>(Vl + row * LS + col * 8) = xv;
+  }
+  __syncthreads();
+
+  if (tid < 2 * D) {
+    const uint16_t* src = (tid < D) ? Kl : Vl;
+    const int d = tid % D;
+    float sum = 0.0f;
+    for (int row = 0; row < n; ++row) sum += bf16_bits_to_f32(src[row * LS + d]);
+    const float mean = sum / (float)n;
+    if (tid < D) {
+      ws.kbar[(bh * s.nb + j) * D + d] = mean;
+      kc[kc_index(d)] = (uint16_t)f32_to_bf16_bits(mean);
+    } else {
+      ws.vbar[(bh * s.nb + j) * D + d] = mean;
+      vc[d * 32 + v_slot(r)] = (uint16_t)f32_to_bf16_bits(mean);
+    }
+  }
+
+  uint16_t* kp = ws.kp + (bh * s.nb + j) * (2LL * HT);
+  uint16_t* vp = ws.vp + (bh * s.nb + j) * (2LL * HT);
+#pragma unroll
+  for (int i = 0; i < CPR / 4; ++i) {
+    const int o = tid + 256 * i;  // output 16-byte chunk, 64 * CPR of them
+    {
+      const int ht = o / (128 * NS), rem = o % (128 * NS);
+      const int kt = rem / (64 * NS), rem2 = rem % (64 * NS);
+      const int ss = rem2 / 64, lane = rem2 % 64;
+      const int row = 32 * ht + 16 * kt + (lane & 15);
+      const int d0 = 32 * ss + 8 * (lane >> 4);
+      *reinterpret_cast<uint4*>(kp + (long long)o * 8) = *reinterpret_cast<const uint4*>(Kl + row * LS + d0);
+    }
+    {
+      const int ht = o / (4 * D), rem = o % (4 * D);
+      const int d = rem >> 2, g = rem & 3;
+      uint32_t w[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t lo = Vl[(32 * ht + v_key(g, 2 * e2)) * LS + d];
+        const uint32_t hi = Vl[(32 * ht + v_key(g, 2 * e2 + 1)) * LS + d];
+        w[e2] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(vp + (long long)o * 8) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
@@ -314,46 +404,40 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
 }
 
 // ---------------------------------------------------------------------------
-// attend: grid B*H*n_b (XCD-aware order), 256 threads = 4 waves of 16 query
-// rows.  Per tile of 64 keys (an exact block, or 64 centroids) K is staged
-// row-major and V transposed in LDS, double-buffered.  Each wave computes
-// S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (lane l holds keys 4(l/16)+i of
-// each 16-key tile for query l%16), so the softmax reductions are in-lane
-// plus two cross-lane steps, and P^T feeds O^T = V^T P^T straight from
-// registers: the MFMA's k index is a free permutation as long as both
-// operands agree, and the V^T reads follow the register order of P^T.
+// attend: one wave per (b, h, query block); grid B*H*n_b in an XCD-aware
+// order.  The wave keeps its 64 query rows as MFMA B operands (Q^T) in
+// registers and walks half tiles of 32 keys: first the two halves of every
+// listed key block, then the centroid half tiles that hold at least one
+// unselected block.  Per half tile:
+//   S^T[key][q] = K Q^T            8 v_mfma_f32_16x16x32_bf16 per 16 queries
+//   online softmax per query       in-lane over 8 keys + 2 cross-lane steps
+//   O^T[d][q] += V^T P^T           8 MFMAs per 16 queries
+// Operands come from the packed buffers in a double-buffered register
+// pipeline (the next half tile is loaded while the current one computes).
 // ---------------------------------------------------------------------------
 template <int D>
-struct AttendCfg {
-  static constexpr int KS = D + 8;        // K tile row stride (bf16)
-  static constexpr int VS = 64 + 8;       // V^T tile row stride (bf16)
-  static constexpr int KT = 64 * KS;
-  static constexpr int VT = D * VS;
-  static constexpr int BUF = KT + VT;     // one stage, bf16 elements
-  static constexpr int NS = D / 32;       // k-steps of Q K^T
-  static constexpr int NDT = D / 16;      // 16-row tiles of O^T
-  static constexpr int CPR = D / 8;       // 16-byte chunks per row
-  static constexpr int NCH = CPR / 4;     // chunks per thread per tensor
-  static constexpr int KPT = CPR / 4;     // consecutive keys per thread (V)
-};
-
-struct TileInfo {
-  const uint16_t* ksrc;  // row 0 of the K (or Kbar) tile
-  const uint16_t* vsrc;
-  long long rstride;     // element stride between rows
-  int nvalid;            // rows that exist
-  int kind;              // 0 exact block, 1 centroid tile
-  int c;                 // block index or centroid tile index
-};
+__device__ __forceinline__ void load_k(uint4 (&kf)[2][D / 32], const uint16_t* __restrict__ base, int lane) {
+  constexpr int NS = D / 32;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int ss = 0; ss < NS; ++ss)
+      kf[kt][ss] = *reinterpret_cast<const uint4*>(base + ((kt * NS + ss) * 64 + lane) * 8);
+}
 
 template <int D>
-__global__ __launch_bounds__(256) void attend_kernel(Shape s, const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ k,
-                                                     const uint16_t* __restrict__ v,
-                                                     uint16_t* __restrict__ out, Workspace ws) {
-  using C = AttendCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
+__device__ __forceinline__ void load_v(uint4 (&vf)[D / 16], const uint16_t* __restrict__ base, int lane) {
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *reinterpret_cast<const uint4*>(base + (16 * dt + l16) * 32 + 8 * g);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __restrict__ q,
+                                                    uint16_t* __restrict__ out, Workspace ws) {
+  constexpr int NS = D / 32, NDT = D / 16, HT = 32 * D;
   __shared__ uint32_t selbits[SA_MAX_BLOCKS / 32];
+  __shared__ int ctile[SA_MAX_BLOCKS / 32];
 
   // Consecutive logical ids go to one XCD (workgroups are dealt to the 8 XCDs
   // round-robin), so one head's query blocks share that XCD's L2.
@@ -365,223 +449,205 @@ __global__ __launch_bounds__(256) void attend_kernel(Shape s, const uint16_t* __
   const int bhi = lid / nb;
   const int h = bhi % s.H, b = bhi / s.H;
   const long long bh = bhi;
+  const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l16 = lane & 15, g = lane >> 4;
-
-  // Q^T fragments (B operand): query a*64 + wave*16 + l16, d = 32 s + 8 g + e.
+  // Q^T fragments: query a*64 + 16 qt + l16, d = 32 ss + 8 g + e.
   const long long in_base = (long long)b * s.isb + (long long)h * s.ish;
-  const int qrow = a * kBlock + wave * 16 + l16;
-  bf16x8 qf[C::NS];
+  bf16x8 qf[4][NS];
 #pragma unroll
-  for (int st = 0; st < C::NS; ++st) {
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (qrow < s.N) x = *reinterpret_cast<const uint4*>(q + in_base + (long long)qrow * s.ist + 32 * st + 8 * g);
-    qf[st] = __builtin_bit_cast(bf16x8, x);
+  for (int qt = 0; qt < 4; ++qt) {
+    const int row = a * kBlock + 16 * qt + l16;
+#pragma unroll
+    for (int ss = 0; ss < NS; ++ss) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (row < s.N) x = *reinterpret_cast<const uint4*>(q + in_base + (long long)row * s.ist + 32 * ss + 8 * g);
+      qf[qt][ss] = __builtin_bit_cast(bf16x8, x);
+    }
   }
 
   int count = nb;
   if (!s.dense) count = min(max(ws.counts[bh * nb + a], 0), nb);
   const int* list = ws.lists + (bh * nb + a) * (long long)nb;
-  const bool cpass = !s.dense && s.centroid && count < nb;
-  const int ctiles = cpass ? s.nbp / 64 : 0;
-  if (cpass) {
-    for (int i = tid; i < s.nbp / 32; i += 256) selbits[i] = 0u;
+  const int nct = s.nbp / 32;  // centroid half tiles
+  int nc = 0;                  // centroid half tiles to visit
+  if (!s.dense && s.centroid && count < nb) {
+    for (int i = lane; i < nct; i += 64) selbits[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < count; i += 256) {
+    for (int i = lane; i < count; i += 64) {
       const int c = list[i];
       if (c >= 0 && c < nb) atomicOr(&selbits[c >> 5], 1u << (c & 31));
     }
-  }
-  const int T = count + ctiles;
-
-  auto tile_info = [&](int t) {
-    TileInfo ti;
-    if (t < count) {
-      const int c = s.dense ? t : list[t];
-      const bool ok = c >= 0 && c < nb;
-      const int cc = ok ? c : 0;
-      ti.ksrc = k + in_base + (long long)cc * kBlock * s.ist;
-      ti.vsrc = v + in_base + (long long)cc * kBlock * s.ist;
-      ti.rstride = s.ist;
-      ti.nvalid = ok ? min(kBlock, s.N - cc * kBlock) : 0;
-      ti.kind = 0;
-      ti.c = cc;
-    } else {
-      const int j = t - count;
-      const long long off = (bh * s.nbp + (long long)j * 64) * D;
-      ti.ksrc = ws.kbar16 + off;
-      ti.vsrc = ws.vbar16 + off;
-      ti.rstride = D;
-      ti.nvalid = 64;
-      ti.kind = 1;
-      ti.c = j;
-    }
-    return ti;
-  };
-
-  uint4 kreg[C::NCH], vreg[C::KPT];
-  const int kcol = tid % C::CPR;
-  const int krow0 = tid / C::CPR;             // K rows krow0 + (256/CPR) i
-  const int vgrp = tid / C::CPR;              // V rows vgrp*KPT + i
-  auto load_tile = [&](const TileInfo& ti) {
-#pragma unroll
-    for (int i = 0; i < C::NCH; ++i) {
-      const int r = krow0 + (256 / C::CPR) * i;
-      kreg[i] = (r < ti.nvalid) ? *reinterpret_cast<const uint4*>(ti.ksrc + (long long)r * ti.rstride + kcol * 8)
-                                : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-      const int r = vgrp * C::KPT + i;
-      vreg[i] = (r < ti.nvalid) ? *reinterpret_cast<const uint4*>(ti.vsrc + (long long)r * ti.rstride + kcol * 8)
-                                : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* Kl = smem + buf * C::BUF;
-    uint16_t* Vl = Kl + C::KT;
-#pragma unroll
-    for (int i = 0; i < C::NCH; ++i) {
-      const int r = krow0 + (256 / C::CPR) * i;
-      *reinterpret_cast<uint4*>(Kl + r * C::KS + kcol * 8) = kreg[i];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t* dst = Vl + (kcol * 8 + e) * C::VS + vgrp * C::KPT;
-      if constexpr (C::KPT == 4) {
-        uint2 w2;
-        w2.x = half16(vreg[0], e) | (half16(vreg[1], e) << 16);
-        w2.y = half16(vreg[2], e) | (half16(vreg[3], e) << 16);
-        *reinterpret_cast<uint2*>(dst) = w2;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = half16(vreg[0], e) | (half16(vreg[1], e) << 16);
+    __syncthreads();
+    // keep the centroid half tiles with at least one unselected, existing block
+    int base = 0;
+    for (int i0 = 0; i0 < nct; i0 += 64) {
+      const int i = i0 + lane;
+      bool keep = false;
+      if (i < nct) {
+        const int valid = min(32, nb - 32 * i);
+        const uint32_t vmask = valid >= 32 ? 0xffffffffu : ((1u << max(valid, 0)) - 1u);
+        keep = (~selbits[i] & vmask) != 0u;
       }
+      const uint64_t m = __ballot(keep);
+      if (keep) ctile[base + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = i;
+      base += __popcll(m);
     }
-  };
-
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x4 acc[C::NDT];
-#pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  TileInfo cur;
-  if (T > 0) {
-    cur = tile_info(0);
-    load_tile(cur);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < T; ++t) {
-    const int buf = t & 1;
-    TileInfo nxt;
-    const bool more = t + 1 < T;
-    if (more) {
-      nxt = tile_info(t + 1);
-      load_tile(nxt);
-    }
-    const uint16_t* Kl = smem + buf * C::BUF;
-    const uint16_t* Vl = Kl + C::KT;
-
-    // S^T tiles: st[kt][i] = K[16 kt + 4 g + i] . Q[l16]
-    f32x4 st[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ss = 0; ss < C::NS; ++ss) {
-        const uint4 x = *reinterpret_cast<const uint4*>(Kl + (16 * kt + l16) * C::KS + 32 * ss + 8 * g);
-        st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), qf[ss], st[kt], 0, 0, 0);
-      }
-    }
-
-    // logits in the log2 domain, masked
-    float x[4][4];
-    if (cur.kind == 0) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * kt + 4 * g + i;
-          x[kt][i] = (key < cur.nvalid) ? st[kt][i] * s.c1 : -INFINITY;
-        }
-    } else {
-      const int cbase = cur.c * 64;
-      const uint64_t bits = (uint64_t)selbits[cbase >> 5] | ((uint64_t)selbits[(cbase >> 5) + 1] << 32);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * kt + 4 * g + i;
-          const int cc = cbase + key;
-          const bool ok = cc < nb && !((bits >> key) & 1ull);
-          const float bias = (cc == nb - 1) ? s.bias_tail : s.bias_full;
-          x[kt][i] = ok ? fmaf(st[kt][i], s.c1, bias) : -INFINITY;
-        }
-    }
-
-    float mx = x[0][0];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-    // Lazy rescale: keep the running max until a row grows by more than 2^8.
-    if (__ballot(mx > m_run + 8.0f)) {
-      const float mnew = fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - mnew);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) acc[dt] *= alpha;
-      m_run = mnew;
-    }
-    const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-
-    bf16x8 pb[2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(x[kt][i] - msub);
-        l_run += p;
-        pb[kt >> 1][(kt & 1) * 4 + i] = (__bf16)p;
-      }
-
-    // O^T += V^T P^T; lane reads V^T[d][32 s + 4 g + 0..3] and [.. + 16 + 0..3]
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        const uint16_t* vp = Vl + (16 * dt + l16) * C::VS + 32 * ss + 4 * g;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-        const uint4 x4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x4), pb[ss], acc[dt], 0, 0, 0);
-      }
-    }
-
-    if (more) {
-      store_tile(buf ^ 1);
-      cur = nxt;
-    }
+    nc = base;
     __syncthreads();
   }
+  const int T = 2 * count + nc;
 
-  float l = l_run;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
-  if (qrow < s.N) {
-    uint16_t* o = out + (long long)b * s.osb + (long long)h * s.osh + (long long)qrow * s.ost;
+  // Half tile t: pointers into the packed buffers.
+  auto bases = [&](int t, const uint16_t*& kb, const uint16_t*& vb) {
+    if (t < 2 * count) {
+      int c = s.dense ? (t >> 1) : list[t >> 1];
+      c = (c >= 0 && c < nb) ? c : 0;
+      const long long off = ((bh * nb + c) * 2 + (t & 1)) * (long long)HT;
+      kb = ws.kp + off;
+      vb = ws.vp + off;
+    } else {
+      const long long off = (bh * nct + ctile[t - 2 * count]) * (long long)HT;
+      kb = ws.kbp + off;
+      vb = ws.vbp + off;
+    }
+  };
+
+  float m_run[4], l_run[4];
+  f32x4 acc[4][NDT];
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-      uint2 w2;
-      w2.x = f32_to_bf16_bits(acc[dt][0] * inv) | (f32_to_bf16_bits(acc[dt][1] * inv) << 16);
-      w2.y = f32_to_bf16_bits(acc[dt][2] * inv) | (f32_to_bf16_bits(acc[dt][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(o + 16 * dt + 4 * g) = w2;
+  for (int qt = 0; qt < 4; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One register buffer per operand: the K loads of half tile t+1 are issued
+  // as soon as the Q K^T products of half tile t are done, the V loads as
+  // soon as its P V products are done, so each load has about half a half
+  // tile of work to arrive.
+  uint4 kf[2][NS], vf[NDT];
+  if (T > 0) {
+    const uint16_t *kb, *vb;
+    bases(0, kb, vb);
+    load_k<D>(kf, kb, lane);
+    load_v<D>(vf, vb, lane);
+  }
+  for (int t = 0; t < T; ++t) {
+    const uint16_t *kb_next = nullptr, *vb_next = nullptr;
+    if (t + 1 < T) bases(t + 1, kb_next, vb_next);
+
+    // S^T: st[qt][kt][i] = K[16 kt + 4 g + i] . Q[16 qt + l16]
+    f32x4 st[4][2];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        st[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ss = 0; ss < NS; ++ss)
+          st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][ss]),
+                                                              qf[qt][ss], st[qt][kt], 0, 0, 0);
+      }
+    if (t + 1 < T) load_k<D>(kf, kb_next, lane);
+
+    // Per-key validity and log2-domain bias; identical for every query.
+    bool full = true;
+    float bias[2][4];
+    bool ok[2][4];
+    if (t < 2 * count) {
+      const int c = s.dense ? (t >> 1) : list[t >> 1];
+      const int nvalid = (c >= 0 && c < nb) ? min(kBlock, s.N - c * kBlock) : 0;
+      full = nvalid == kBlock;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ok[kt][i] = 32 * (t & 1) + 16 * kt + 4 * g + i < nvalid;
+          bias[kt][i] = 0.0f;
+        }
+    } else {
+      full = false;
+      const int J = ctile[t - 2 * count];
+      const uint32_t bits = selbits[J];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * kt + 4 * g + i;
+          const int cc = 32 * J + r;
+          ok[kt][i] = cc < nb && !((bits >> r) & 1u);
+          bias[kt][i] = (cc == nb - 1) ? s.bias_tail : s.bias_full;
+        }
+    }
+
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      float x[2][4];
+      float mx = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[kt][i] = st[qt][kt][i] * s.c1;
+            mx = fmaxf(mx, x[kt][i]);
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[kt][i] = ok[kt][i] ? fmaf(st[qt][kt][i], s.c1, bias[kt][i]) : -INFINITY;
+            mx = fmaxf(mx, x[kt][i]);
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // Lazy rescale: keep the running max until a row grows by more than 2^8.
+      if (__ballot(mx > m_run[qt] + 8.0f)) {
+        const float mnew = fmaxf(m_run[qt], mx);
+        const float alpha = (m_run[qt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[qt] - mnew);
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] *= alpha;
+        m_run[qt] = mnew;
+      }
+      const float msub = (m_run[qt] == -INFINITY) ? 0.0f : m_run[qt];
+      bf16x8 pb;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(x[kt][i] - msub);
+          l_run[qt] += p;
+          pb[kt * 4 + i] = (__bf16)p;
+        }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]), pb,
+                                                             acc[qt][dt], 0, 0, 0);
+    }
+    if (t + 1 < T) load_v<D>(vf, vb_next, lane);
+  }
+
+  const long long out_base = (long long)b * s.osb + (long long)h * s.osh;
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    float l = l_run[qt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+    const int row = a * kBlock + 16 * qt + l16;
+    if (row < s.N) {
+      uint16_t* o = out + out_base + (long long)row * s.ost;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        uint2 w2;
+        w2.x = f32_to_bf16_bits(acc[qt][dt][0] * inv) | (f32_to_bf16_bits(acc[qt][dt][1] * inv) << 16);
+        w2.y = f32_to_bf16_bits(acc[qt][dt][2] * inv) | (f32_to_bf16_bits(acc[qt][dt][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(o + 16 * dt + 4 * g) = w2;
+      }
     }
   }
 }
@@ -599,17 +665,26 @@ hipError_t launch_select_t(const Shape& s, const Workspace& ws, hipStream_t stre
 
 }  // namespace
 
-hipError_t launch_pool(const Shape& s, const void* q, const void* k, const void* v, const Workspace& ws,
-                       hipStream_t stream) {
+hipError_t launch_pool_q(const Shape& s, const void* q, const Workspace& ws, hipStream_t stream) {
   const int hg = 128 / (s.D / 8);
-  dim3 grid(s.nbp, 3, s.B * ((s.H + hg - 1) / hg));
+  dim3 grid(s.nb, 1, s.B * ((s.H + hg - 1) / hg));
   const auto* qq = static_cast<const uint16_t*>(q);
+  if (s.D == 128)
+    hipLaunchKernelGGL(pool_q_kernel<128>, grid, dim3(256), 0, stream, s, qq, ws);
+  else
+    hipLaunchKernelGGL(pool_q_kernel<64>, grid, dim3(256), 0, stream, s, qq, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_kv(const Shape& s, const void* k, const void* v, const Workspace& ws,
+                          hipStream_t stream) {
+  dim3 grid(s.nbp, s.H, s.B);
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
   if (s.D == 128)
-    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, stream, s, qq, kk, vv, ws);
+    hipLaunchKernelGGL(pack_kv_kernel<128>, grid, dim3(256), 0, stream, s, kk, vv, ws);
   else
-    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, stream, s, qq, kk, vv, ws);
+    hipLaunchKernelGGL(pack_kv_kernel<64>, grid, dim3(256), 0, stream, s, kk, vv, ws);
   return hipGetLastError();
 }
 
@@ -619,17 +694,14 @@ hipError_t launch_select(const Shape& s, const Workspace& ws, hipStream_t stream
   return big ? launch_select_t<64, 8>(s, ws, stream) : launch_select_t<64, 16>(s, ws, stream);
 }
 
-hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v, void* out,
-                         const Workspace& ws, hipStream_t stream) {
+hipError_t launch_attend(const Shape& s, const void* q, void* out, const Workspace& ws, hipStream_t stream) {
   dim3 grid((unsigned)((long long)s.B * s.H * s.nb));
   const auto* qq = static_cast<const uint16_t*>(q);
-  const auto* kk = static_cast<const uint16_t*>(k);
-  const auto* vv = static_cast<const uint16_t*>(v);
   auto* oo = static_cast<uint16_t*>(out);
   if (s.D == 128)
-    hipLaunchKernelGGL(attend_kernel<128>, grid, dim3(256), 0, stream, s, qq, kk, vv, oo, ws);
+    hipLaunchKernelGGL(attend_kernel<128>, grid, dim3(64), 0, stream, s, qq, oo, ws);
   else
-    hipLaunchKernelGGL(attend_kernel<64>, grid, dim3(256), 0, stream, s, qq, kk, vv, oo, ws);
+    hipLaunchKernelGGL(attend_kernel<64>, grid, dim3(64), 0, stream, s, qq, oo, ws);
   return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ extern "C" {
 
 #define SA_BLOCK 64          /* rows per query / key block */
 #define SA_MAX_BLOCKS 2048   /* largest supported n_b = ceil(N / 64) */
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 
 /* Routing modes (sparse_attn_params.route). */
 #define SA_ROUTE_TAU 0   /* S >= mean + tau * std; tau = -inf is the dense path */
@@ -89,18 +89,33 @@ typedef struct sparse_attn_params {
 
 typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
 
-/* Byte offsets of the workspace sections (all 256-byte aligned).  After
- * sparse_attn_pool: qbar, kbar, vbar hold the fp32 block means
- * [B, H, n_b, D]; kbar_bf16 and vbar_bf16 hold them rounded to bf16
- * (round to nearest even) as [B, H, n_bp, D], n_bp = n_b rounded up to 64,
- * padding rows zero.  After sparse_attn_select: counts [B, H, n_b] int32
- * holds the number of selected key blocks per query block and lists
- * [B, H, n_b, n_b] int32 holds them in ascending order in the first `count`
- * entries of each row (the rest of the row is unspecified). */
+/* Byte offsets of the workspace sections (all 256-byte aligned).
+ *
+ * After sparse_attn_pool:
+ *   qbar, kbar, vbar  fp32 [B, H, n_b, D]: the block means of Q, K, V.
+ *   k_packed          bf16, one 64*D-element tile per (b, h, block): the
+ *                     block's K rows (zero past N) in MFMA operand order,
+ *                     as two 32-row half tiles; in a half tile, element
+ *                     ((kt*NS + ss)*64 + lane)*8 + e holds
+ *                     K[16 kt + lane%16][32 ss + 8 (lane/16) + e], NS = D/32.
+ *   v_packed          bf16, same tiling for V^T: in a half tile, element
+ *                     d*32 + 8 g + e holds V[key(g, e)][d], where
+ *                     key(g, e) = 4 g + e for e < 4 and 16 + 4 g + e - 4
+ *                     otherwise.
+ *   kbar_packed,      bf16 centroids (the means rounded to nearest even),
+ *   vbar_packed       [B, H, n_bp/32] half tiles in the same two orders;
+ *                     block c is row c % 32 of half tile c / 32; rows of
+ *                     blocks >= n_b are zero (n_bp = n_b rounded up to 64).
+ * After sparse_attn_select:
+ *   counts            int32 [B, H, n_b]: selected key blocks per query block.
+ *   lists             int32 [B, H, n_b, n_b]: the selected key blocks in
+ *                     ascending order in the first `count` entries of each
+ *                     row (the rest of the row is unspecified). */
 typedef struct sparse_attn_ws_layout {
   uint64_t total_bytes;
   uint64_t qbar, kbar, vbar;
-  uint64_t kbar_bf16, vbar_bf16;
+  uint64_t k_packed, v_packed;
+  uint64_t kbar_packed, vbar_packed;
   uint64_t counts, lists;
   int32_t n_blocks;        /* n_b */
   int32_t n_blocks_padded; /* n_bp */
@@ -121,16 +136,17 @@ void sparse_attn_plan_destroy(sparse_attn_plan* plan);
 /* Fills *layout for the plan's shape (host only). */
 int sparse_attn_workspace_layout(const sparse_attn_plan* plan, sparse_attn_ws_layout* layout);
 
-/* Full forward: pool, select and attend (or attend alone on the dense path)
- * enqueued on `stream` (a hipStream_t; NULL is the null stream).  q, k, v
- * are read-only bf16 device pointers and may alias one another; out is a
- * bf16 device pointer that must not overlap them.  ws points to at least
- * layout.total_bytes of device memory (256-byte aligned), ws_bytes is its
- * size; its contents on entry do not matter. */
+/* Full forward: pool, select and attend (pool and attend alone on the dense
+ * path) enqueued on `stream` (a hipStream_t; NULL is the null stream).
+ * q, k, v are read-only bf16 device pointers and may alias one another; out
+ * is a bf16 device pointer that must not overlap them or ws.  ws points to at
+ * least layout.total_bytes of device memory (256-byte aligned), ws_bytes is
+ * its size; its contents on entry do not matter. */
 int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
                         void* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Step 1 alone: writes qbar, kbar, vbar, kbar_bf16 and vbar_bf16. */
+/* Step 1 alone: block means of Q, K, V and the packed K, V^T and centroid
+ * tiles (every section listed under "After sparse_attn_pool"). */
 int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
                      void* ws, size_t ws_bytes, void* stream);
 
@@ -140,13 +156,13 @@ int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k,
 int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, void* stream);
 
 /* Step 4 alone: exact attention over each query block's list and centroid
- * terms for every other block, from counts, lists and the bf16 centroids in
- * ws.  A caller may write its own lists: entries must be distinct block
- * indices in [0, n_b) (out-of-range entries are skipped), counts in
- * [0, n_b]; a query block whose count is n_b gets no centroid term.  On the
- * dense path the lists are not read. */
-int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
-                       void* out, void* ws, size_t ws_bytes, void* stream);
+ * terms for every other block, reading q and, from ws, the packed tiles,
+ * counts and lists.  A caller may write its own lists: entries must be
+ * distinct block indices in [0, n_b) (out-of-range entries are treated as
+ * block 0 with no valid key), counts in [0, n_b]; a query block whose count
+ * is n_b gets no centroid term.  On the dense path lists are not read. */
+int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, void* out, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Static message for an error code. */
 const char* sparse_attn_strerror(int code);

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.sparse_attn_abi_version() == 1
+    assert lib.sparse_attn_abi_version() == 2
 
 
 def _params(**kw):
@@ -114,9 +114,11 @@ def test_workspace_layout_matches_documented_sizes():
     nb = 16
     assert L["n_blocks"] == nb and L["n_blocks_padded"] == 64
     assert L["tail_rows"] == 1000 - 64 * 15 and L["prefix_blocks"] == 2 and L["dense"] == 0
-    offs = sorted((L[n], n) for n in ("qbar", "kbar", "vbar", "kbar_bf16", "vbar_bf16", "counts", "lists"))
+    names = ("qbar", "kbar", "vbar", "k_packed", "v_packed", "kbar_packed", "vbar_packed", "counts", "lists")
+    offs = sorted((L[n], n) for n in names)
     sizes = dict(qbar=2 * 3 * nb * 128 * 4, kbar=2 * 3 * nb * 128 * 4, vbar=2 * 3 * nb * 128 * 4,
-                 kbar_bf16=2 * 3 * 64 * 128 * 2, vbar_bf16=2 * 3 * 64 * 128 * 2,
+                 k_packed=2 * 3 * nb * 64 * 128 * 2, v_packed=2 * 3 * nb * 64 * 128 * 2,
+                 kbar_packed=2 * 3 * 64 * 128 * 2, vbar_packed=2 * 3 * 64 * 128 * 2,
                  counts=2 * 3 * nb * 4, lists=2 * 3 * nb * nb * 4)
     for (o, n), (o2, _) in zip(offs, offs[1:] + [(L["total_bytes"], "end")]):
         assert o % 256 == 0
@@ -143,6 +145,7 @@ def test_call_validation_before_launch(lib):
     need = plan.workspace_bytes
     fake = 1 << 20  # never dereferenced: validation fails first
     f = lib.sparse_attn_forward
+    lib.sparse_attn_attend.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]
     assert f(h, None, fake, fake, fake, fake, need, None) == SA_EINVAL
     assert f(h, fake + 2, fake, fake, fake, fake, need, None) == SA_EALIGN
     assert f(h, fake, fake, fake, fake, fake + 16, need, None) == SA_EALIGN
@@ -151,7 +154,8 @@ def test_call_validation_before_launch(lib):
     assert f(None, fake, fake, fake, fake, fake, need, None) == SA_EINVAL
     assert lib.sparse_attn_select(h, None, need, None) == SA_EINVAL
     assert lib.sparse_attn_pool(h, fake, fake, fake, fake, need - 256, None) == SA_EWORKSPACE
-    assert lib.sparse_attn_attend(h, fake, fake, fake, None, fake, need, None) == SA_EINVAL
+    assert lib.sparse_attn_attend(h, fake, None, fake, need, None) == SA_EINVAL
+    assert lib.sparse_attn_attend(h, fake, fake, fake, need - 1, None) == SA_EWORKSPACE
 
 
 def test_binding_rejects_bad_tensors():

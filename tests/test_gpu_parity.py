@@ -137,22 +137,50 @@ def full_parity(q, k, v, **kw):
 # ----------------------------------------------------------------- pooling
 
 
+def _unpack_k(tile, D):
+    """Packed K half tile (32*D,) -> [32, D] per the order in sparse_attn.h."""
+    NS = D // 32
+    t = tile.reshape(2, NS, 4, 16, 8)  # [kt, ss, g, l16, e]
+    return t.transpose(0, 3, 1, 2, 4).reshape(32, D)  # row 16 kt + l16, col 32 ss + 8 g + e
+
+
+def _unpack_vt(tile, D):
+    """Packed V^T half tile (32*D,) -> V [32 keys, D]."""
+    t = tile.reshape(D, 4, 8)  # [d, g, e]
+    keys = np.array([[4 * g + e if e < 4 else 16 + 4 * g + e - 4 for e in range(8)] for g in range(4)])
+    v = np.empty((32, D), dtype=tile.dtype)
+    v[keys.reshape(-1)] = t.reshape(D, 32).T
+    return v
+
+
 @pytest.mark.parametrize("N,D", [(1024, 64), (200, 128), (38247 - 37 * 1024, 128)])
-def test_pooled_means(N, D):
+def test_pooled_means_and_packed_tiles(N, D):
     q, k, v = inputs.iid(2, N, 3, D, seed=N)
     run = GpuRun(q, k, v, tau=1.0)
-    qb, kb, vb, kb16, vb16 = (t.float().cpu().numpy() for t in run.plan.pooled_views(run.ws))
+    qb, kb, vb = (t.float().cpu().numpy() for t in run.plan.pooled_views(run.ws))
     for got, x in ((qb, q), (kb, k), (vb, v)):
         xf = _f32(x).astype(np.float64)
         ref = O.pool(xf)
         bound = 2 * 64 * 2.0**-24 * np.abs(xf).max()
         assert np.abs(got - ref).max() <= bound
-    nb = qb.shape[2]
-    # bf16 copies are the fp32 means rounded to nearest even; padding rows are zero
-    for got16, f in ((kb16, kb), (vb16, vb)):
-        want = _f32(inputs.f32_to_bf16_bits(f))
-        np.testing.assert_array_equal(got16[:, :, :nb], want)
-        assert (got16[:, :, nb:] == 0).all()
+    kp, vp, kbp, vbp = (t.float().cpu().numpy() for t in run.plan.packed_views(run.ws))
+    B, H, nb = qb.shape[:3]
+    kf, vf = _f32(k), _f32(v)
+    for b in range(B):
+        for h in range(H):
+            for c in (0, nb // 2, nb - 1):
+                for ht in range(2):
+                    rows = np.arange(c * 64 + 32 * ht, c * 64 + 32 * ht + 32)
+                    want_k = np.where((rows < N)[:, None], kf[b, np.minimum(rows, N - 1), h], 0)
+                    want_v = np.where((rows < N)[:, None], vf[b, np.minimum(rows, N - 1), h], 0)
+                    np.testing.assert_array_equal(_unpack_k(kp[b, h, c, ht], D), want_k)
+                    np.testing.assert_array_equal(_unpack_vt(vp[b, h, c, ht], D), want_v)
+            # centroids: fp32 means rounded to nearest even, rows past n_b zero
+            ck = np.concatenate([_unpack_k(t, D) for t in kbp[b, h]])
+            cv = np.concatenate([_unpack_vt(t, D) for t in vbp[b, h]])
+            np.testing.assert_array_equal(ck[:nb], _f32(inputs.f32_to_bf16_bits(kb[b, h])))
+            np.testing.assert_array_equal(cv[:nb], _f32(inputs.f32_to_bf16_bits(vb[b, h])))
+            assert (ck[nb:] == 0).all() and (cv[nb:] == 0).all()
 
 
 # ---------------------------------------------------- small, every output row
@@ -248,7 +276,7 @@ def test_injected_lists_through_attend():
     counts.copy_(torch.from_numpy(cnt))
     lists.copy_(torch.from_numpy(lst))
     out = torch.empty_like(tq)
-    plan.attend(tq, tk, tv, out, ws)
+    plan.attend(tq, out, ws)
     torch.cuda.synchronize()
     ref, _ = O.forward(_f32(q), _f32(k), _f32(v), mask=sel)
     check_output(out.float().cpu().numpy().astype(np.float64), ref, "injected")
