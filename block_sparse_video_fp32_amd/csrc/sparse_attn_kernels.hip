@@ -522,23 +522,33 @@ __global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __r
     for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One register buffer per operand: the K loads of half tile t+1 are issued
-  // as soon as the Q K^T products of half tile t are done, the V loads as
-  // soon as its P V products are done, so each load has about half a half
-  // tile of work to arrive.
-  uint4 kf[2][NS], vf[NDT];
-  if (T > 0) {
-    const uint16_t *kb, *vb;
-    bases(0, kb, vb);
-    load_k<D>(kf, kb, lane);
-    load_v<D>(vf, vb, lane);
-  }
-  for (int t = 0; t < T; ++t) {
-    const uint16_t *kb_next = nullptr, *vb_next = nullptr;
-    if (t + 1 < T) bases(t + 1, kb_next, vb_next);
-
-    // S^T: st[qt][kt][i] = K[16 kt + 4 g + i] . Q[16 qt + l16]
-    f32x4 st[4][2];
+  // Additive per-key term of half tile t in the log2 domain: 0 for a valid
+  // key of an exact block, log2(n_c) (or 0 without the log-mass bias) for an
+  // unselected centroid, -inf for keys past N, selected centroids and
+  // centroid rows past n_b.  The same for every query.
+  auto key_bias = [&](int t, float (&kb)[2][4]) {
+    if (t < 2 * count) {
+      const int c = s.dense ? (t >> 1) : list[t >> 1];
+      const int nvalid = (c >= 0 && c < nb) ? min(kBlock, s.N - c * kBlock) : 0;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kb[kt][i] = (32 * (t & 1) + 16 * kt + 4 * g + i < nvalid) ? 0.0f : -INFINITY;
+    } else {
+      const int J = ctile[t - 2 * count];
+      const uint32_t bits = selbits[J];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * kt + 4 * g + i;
+          const int cc = 32 * J + r;
+          const bool ok = cc < nb && !((bits >> r) & 1u);
+          kb[kt][i] = ok ? ((cc == nb - 1) ? s.bias_tail : s.bias_full) : -INFINITY;
+        }
+    }
+  };
+  auto qk = [&](const uint4 (&kf)[2][NS], f32x4 (&st)[4][2]) {
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
@@ -549,94 +559,106 @@ __global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __r
           st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][ss]),
                                                               qf[qt][ss], st[qt][kt], 0, 0, 0);
       }
-    if (t + 1 < T) load_k<D>(kf, kb_next, lane);
+  };
 
-    // Per-key validity and log2-domain bias; identical for every query.
-    bool full = true;
-    float bias[2][4];
-    bool ok[2][4];
-    if (t < 2 * count) {
-      const int c = s.dense ? (t >> 1) : list[t >> 1];
-      const int nvalid = (c >= 0 && c < nb) ? min(kBlock, s.N - c * kBlock) : 0;
-      full = nvalid == kBlock;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ok[kt][i] = 32 * (t & 1) + 16 * kt + 4 * g + i < nvalid;
-          bias[kt][i] = 0.0f;
-        }
-    } else {
-      full = false;
-      const int J = ctile[t - 2 * count];
-      const uint32_t bits = selbits[J];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * kt + 4 * g + i;
-          const int cc = 32 * J + r;
-          ok[kt][i] = cc < nb && !((bits >> r) & 1u);
-          bias[kt][i] = (cc == nb - 1) ? s.bias_tail : s.bias_full;
-        }
-    }
-
+  // Software pipeline over half tiles.  Iteration t: logits and row maxima
+  // of t (VALU, overlapping the P V products of t-1 still in the MFMA pipe),
+  // the rare rescale, exponentials of t overlapping Q K^T of t+1, then
+  // P V of t.  K of t+2 is requested once Q K^T of t+1 has read its
+  // registers, V of t+1 once P V of t has; each load has an iteration to
+  // arrive.  Indices past the end are clamped (a redundant last Q K^T).
+  uint4 kf[2][NS], vf[NDT];
+  f32x4 st[4][2];
+  if (T > 0) {
+    const uint16_t *kb0, *vb0;
+    bases(0, kb0, vb0);
+    load_k<D>(kf, kb0, lane);
+    load_v<D>(vf, vb0, lane);
+    qk(kf, st);
+    bases(min(1, T - 1), kb0, vb0);
+    load_k<D>(kf, kb0, lane);
+  }
+  for (int t = 0; t < T; ++t) {
+    float kbias[2][4];
+    key_bias(t, kbias);
+    float x[4][2][4], mx[4];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
-      float x[2][4];
-      float mx = -INFINITY;
-      if (full) {
+      float m = -INFINITY;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[kt][i] = st[qt][kt][i] * s.c1;
-            mx = fmaxf(mx, x[kt][i]);
-          }
-      } else {
+        for (int i = 0; i < 4; ++i) {
+          x[qt][kt][i] = fmaf(st[qt][kt][i], s.c1, kbias[kt][i]);
+          m = fmaxf(m, x[qt][kt][i]);
+        }
+      // max over the four lanes that hold this query (lane ^ 16, lane ^ 32)
+      const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      m = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+      const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      mx[qt] = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+    }
+    // Lazy rescale: keep a running max until a row grows by more than 2^8.
+    bool grow = false;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+    for (int qt = 0; qt < 4; ++qt) grow |= mx[qt] > m_run[qt] + 8.0f;
+    if (__ballot(grow)) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[kt][i] = ok[kt][i] ? fmaf(st[qt][kt][i], s.c1, bias[kt][i]) : -INFINITY;
-            mx = fmaxf(mx, x[kt][i]);
-          }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Lazy rescale: keep the running max until a row grows by more than 2^8.
-      if (__ballot(mx > m_run[qt] + 8.0f)) {
-        const float mnew = fmaxf(m_run[qt], mx);
+      for (int qt = 0; qt < 4; ++qt) {
+        const float mnew = fmaxf(m_run[qt], mx[qt]);
         const float alpha = (m_run[qt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[qt] - mnew);
         l_run[qt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] *= alpha;
         m_run[qt] = mnew;
       }
+    }
+    bf16x8 pb[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
       const float msub = (m_run[qt] == -INFINITY) ? 0.0f : m_run[qt];
-      bf16x8 pb;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(x[kt][i] - msub);
+          const float p = __builtin_amdgcn_exp2f(x[qt][kt][i] - msub);
           l_run[qt] += p;
-          pb[kt * 4 + i] = (__bf16)p;
+          pb[qt][kt * 4 + i] = (__bf16)p;
         }
+    }
+    // Q K^T of the next half tile (K already loaded), then K of t+2.
+    qk(kf, st);
+    {
+      const uint16_t *kb2, *vb2;
+      bases(min(t + 2, T - 1), kb2, vb2);
+      load_k<D>(kf, kb2, lane);
+    }
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]), pb,
+        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]), pb[qt],
                                                              acc[qt][dt], 0, 0, 0);
+    {
+      const uint16_t *kb1, *vb1;
+      bases(min(t + 1, T - 1), kb1, vb1);
+      load_v<D>(vf, vb1, lane);
     }
-    if (t + 1 < T) load_v<D>(vf, vb_next, lane);
+  }
+
+  // Row sums: add the partial sums of the four lanes holding each query.
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l_run[qt]), __float_as_uint(l_run[qt]), false, false);
+    const float l2 = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
+    l_run[qt] = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
   }
 
   const long long out_base = (long long)b * s.osb + (long long)h * s.osh;
 #pragma unroll
   for (int qt = 0; qt < 4; ++qt) {
-    float l = l_run[qt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = l_run[qt];
     const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
     const int row = a * kBlock + 16 * qt + l16;
     if (row < s.N) {
