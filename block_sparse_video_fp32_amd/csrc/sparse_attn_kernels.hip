@@ -497,56 +497,50 @@ __global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __r
   }
   const int T = 2 * count + nc;
 
-  // Half tile t: pointers into the packed buffers.
-  auto bases = [&](int t, const uint16_t*& kb, const uint16_t*& vb) {
-    if (t < 2 * count) {
-      int c = s.dense ? (t >> 1) : list[t >> 1];
-      c = (c >= 0 && c < nb) ? c : 0;
-      const long long off = ((bh * nb + c) * 2 + (t & 1)) * (long long)HT;
-      kb = ws.kp + off;
-      vb = ws.vp + off;
-    } else {
-      const long long off = (bh * nct + ctile[t - 2 * count]) * (long long)HT;
-      kb = ws.kbp + off;
-      vb = ws.vbp + off;
-    }
+  // Half tile t: pointers into the packed buffers and the additive per-key
+  // term in the log2 domain (0 for a valid key of an exact block, log2(n_c)
+  // or 0 for an unselected centroid, -inf for keys past N, selected
+  // centroids and centroid rows past n_b), the same for every query.  Both
+  // are computed without branches so that the loop body stays one block.
+  const uint16_t* kp_bh = ws.kp + bh * nb * 2LL * HT;
+  const uint16_t* vp_bh = ws.vp + bh * nb * 2LL * HT;
+  const uint16_t* kc_bh = ws.kbp + bh * nct * (long long)HT;
+  const uint16_t* vc_bh = ws.vbp + bh * nct * (long long)HT;
+  const int nexact = 2 * count;
+  auto tile_off = [&](int t, bool& centroid, int& c) {
+    centroid = t >= nexact;
+    const int ce = s.dense ? (t >> 1) : list[min(t, nexact - 1) >> 1];
+    const int ci = ctile[max(t - nexact, 0)];
+    c = centroid ? ci : ((ce >= 0 && ce < nb) ? ce : -1);
+    const long long e_off = ((long long)max(c, 0) * 2 + (t & 1)) * HT;
+    const long long c_off = (long long)ci * HT;
+    return centroid ? c_off : e_off;
   };
-
-  float m_run[4], l_run[4];
-  f32x4 acc[4][NDT];
-#pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // Additive per-key term of half tile t in the log2 domain: 0 for a valid
-  // key of an exact block, log2(n_c) (or 0 without the log-mass bias) for an
-  // unselected centroid, -inf for keys past N, selected centroids and
-  // centroid rows past n_b.  The same for every query.
+  auto tile_ptrs = [&](int t, const uint16_t*& kb, const uint16_t*& vb) {
+    bool centroid;
+    int c;
+    const long long off = tile_off(t, centroid, c);
+    kb = (centroid ? kc_bh : kp_bh) + off;
+    vb = (centroid ? vc_bh : vp_bh) + off;
+  };
   auto key_bias = [&](int t, float (&kb)[2][4]) {
-    if (t < 2 * count) {
-      const int c = s.dense ? (t >> 1) : list[t >> 1];
-      const int nvalid = (c >= 0 && c < nb) ? min(kBlock, s.N - c * kBlock) : 0;
+    bool centroid;
+    int c;
+    tile_off(t, centroid, c);
+    // exact: valid keys 32*(t&1) + r < nvalid; centroid: r unselected and 32c + r < nb
+    const int nvalid = (c >= 0) ? min(kBlock, s.N - c * kBlock) : 0;
+    const uint32_t sel = centroid ? selbits[c] : 0u;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kb[kt][i] = (32 * (t & 1) + 16 * kt + 4 * g + i < nvalid) ? 0.0f : -INFINITY;
-    } else {
-      const int J = ctile[t - 2 * count];
-      const uint32_t bits = selbits[J];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * kt + 4 * g + i;
-          const int cc = 32 * J + r;
-          const bool ok = cc < nb && !((bits >> r) & 1u);
-          kb[kt][i] = ok ? ((cc == nb - 1) ? s.bias_tail : s.bias_full) : -INFINITY;
-        }
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * kt + 4 * g + i;
+        const int cc = 32 * c + r;
+        const bool ok_e = 32 * (t & 1) + r < nvalid;
+        const bool ok_c = cc < nb && !((sel >> r) & 1u);
+        const float bc = (cc == nb - 1) ? s.bias_tail : s.bias_full;
+        kb[kt][i] = centroid ? (ok_c ? bc : -INFINITY) : (ok_e ? 0.0f : -INFINITY);
+      }
   };
   auto qk = [&](const uint4 (&kf)[2][NS], f32x4 (&st)[4][2]) {
 #pragma unroll
@@ -561,104 +555,153 @@ __global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __r
       }
   };
 
-  // Software pipeline over half tiles.  Iteration t: logits and row maxima
-  // of t (VALU, overlapping the P V products of t-1 still in the MFMA pipe),
-  // the rare rescale, exponentials of t overlapping Q K^T of t+1, then
-  // P V of t.  K of t+2 is requested once Q K^T of t+1 has read its
-  // registers, V of t+1 once P V of t has; each load has an iteration to
-  // arrive.  Indices past the end are clamped (a redundant last Q K^T).
-  uint4 kf[2][NS], vf[NDT];
-  f32x4 st[4][2];
-  if (T > 0) {
-    const uint16_t *kb0, *vb0;
-    bases(0, kb0, vb0);
-    load_k<D>(kf, kb0, lane);
-    load_v<D>(vf, vb0, lane);
-    qk(kf, st);
-    bases(min(1, T - 1), kb0, vb0);
-    load_k<D>(kf, kb0, lane);
-  }
-  for (int t = 0; t < T; ++t) {
-    float kbias[2][4];
-    key_bias(t, kbias);
-    float x[4][2][4], mx[4];
+  // Softmax reference.  Every logit x of query row q is scored as
+  // p = exp2(x - mref[q]) with a fixed mref[q]: the exact maximum over the
+  // row's first half tile plus 32 (log2 units).  Terms of that tile then lie
+  // below 2^-32 and the row's largest term is at least 2^-32, far inside the
+  // fp32 / bf16 exponent range, and no running maximum or rescaling of the
+  // accumulators is needed.  The ratio acc / l is independent of mref, so
+  // this is the same softmax up to rounding.  Should a later term exceed
+  // mref by so much that the row sum leaves [0, 2^100] (or is not finite),
+  // the query block is recomputed with the exact row maxima from a
+  // Q K^T-only pass.
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  f32x4 acc[4][NDT], lacc[4];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // Is half tile t an exact tile with every key valid (no per-key term)?
+  auto plain_tile = [&](int t) {
+    if (t >= nexact) return false;
+    const int c = s.dense ? (t >> 1) : list[t >> 1];
+    return c >= 0 && c < nb && (c < nb - 1 || (t & 1) * 32 + 32 <= s.tail);
+  };
+  // Row maxima of one half tile's logits (used for the reference only).
+  auto row_max = [&](const f32x4 (&st)[4][2], int tt, float (&mx)[4]) {
+    float kb[2][4];
+    key_bias(tt, kb);
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
       float m = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[qt][kt][i] = fmaf(st[qt][kt][i], s.c1, kbias[kt][i]);
-          m = fmaxf(m, x[qt][kt][i]);
-        }
-      // max over the four lanes that hold this query (lane ^ 16, lane ^ 32)
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaf(st[qt][kt][i], s.c1, kb[kt][i]));
       const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
       m = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
       const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
       mx[qt] = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
     }
-    // Lazy rescale: keep a running max until a row grows by more than 2^8.
-    bool grow = false;
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) grow |= mx[qt] > m_run[qt] + 8.0f;
-    if (__ballot(grow)) {
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        const float mnew = fmaxf(m_run[qt], mx[qt]);
-        const float alpha = (m_run[qt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[qt] - mnew);
-        l_run[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] *= alpha;
-        m_run[qt] = mnew;
-      }
-    }
-    bf16x8 pb[4];
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      const float msub = (m_run[qt] == -INFINITY) ? 0.0f : m_run[qt];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(x[qt][kt][i] - msub);
-          l_run[qt] += p;
-          pb[qt][kt * 4 + i] = (__bf16)p;
-        }
-    }
-    // Q K^T of the next half tile (K already loaded), then K of t+2.
-    qk(kf, st);
+  };
+
+  // Pipeline state: K of the next half tile in kf, V of the current one in
+  // vf, S^T of the current one in the "current" st buffer.
+  uint4 kf[2][NS], vf[NDT];
+  f32x4 stA[4][2], stB[4][2];
+  auto prologue = [&]() {
+    const uint16_t *kb0, *vb0;
+    tile_ptrs(0, kb0, vb0);
+    load_k<D>(kf, kb0, lane);
+    load_v<D>(vf, vb0, lane);
+    qk(kf, stA);
+    tile_ptrs(min(1, T - 1), kb0, vb0);
+    load_k<D>(kf, kb0, lane);
+  };
+  // One iteration: Q K^T of t+1 is issued first so that the exponentials of
+  // t (VALU) run while it is in the MFMA pipe; then P V of t and the row
+  // sums (an MFMA against ones); K of t+2 and V of t+1 are requested as soon
+  // as their registers are free.  Indices past the end are clamped (a
+  // redundant last Q K^T).
+  auto step = [&](int t, const f32x4 (&st)[4][2], f32x4 (&st_next)[4][2], const float (&mref)[4]) {
+    qk(kf, st_next);
     {
       const uint16_t *kb2, *vb2;
-      bases(min(t + 2, T - 1), kb2, vb2);
+      tile_ptrs(min(t + 2, T - 1), kb2, vb2);
       load_k<D>(kf, kb2, lane);
     }
+    bf16x8 pb[4];
+    if (plain_tile(t)) {
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt)
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pb[qt][kt * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[qt][kt][i], s.c1, -mref[qt]));
+    } else {
+      float kb[2][4];
+      key_bias(t, kb);
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pb[qt][kt * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[qt][kt][i], s.c1, kb[kt][i] - mref[qt]));
+    }
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]), pb[qt],
                                                              acc[qt][dt], 0, 0, 0);
+      lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qt], lacc[qt], 0, 0, 0);
+    }
     {
       const uint16_t *kb1, *vb1;
-      bases(min(t + 1, T - 1), kb1, vb1);
+      tile_ptrs(min(t + 1, T - 1), kb1, vb1);
       load_v<D>(vf, vb1, lane);
     }
-  }
+  };
+  auto run = [&](const float (&mref)[4]) {
+    for (int t = 0; t < T; t += 2) {
+      step(t, stA, stB, mref);
+      if (t + 1 < T) step(t + 1, stB, stA, mref);
+    }
+  };
 
-  // Row sums: add the partial sums of the four lanes holding each query.
+  float mref[4] = {0.f, 0.f, 0.f, 0.f};
+  zero_acc();
+  if (T > 0) {
+    prologue();
+    float mx[4];
+    row_max(stA, 0, mx);
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l_run[qt]), __float_as_uint(l_run[qt]), false, false);
-    const float l2 = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
-    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
-    l_run[qt] = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+    for (int qt = 0; qt < 4; ++qt) mref[qt] = (mx[qt] == -INFINITY) ? 0.0f : mx[qt] + 32.0f;
+    run(mref);
+    bool bad = false;
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) bad |= !(lacc[qt][0] <= 0x1p100f);
+    if (__ballot(bad)) {
+      // Exact row maxima over every half tile, then the same computation.
+      float mtrue[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      for (int t = 0; t < T; ++t) {
+        const uint16_t *kb0, *vb0;
+        tile_ptrs(t, kb0, vb0);
+        load_k<D>(kf, kb0, lane);
+        qk(kf, stA);
+        float mx2[4];
+        row_max(stA, t, mx2);
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) mtrue[qt] = fmaxf(mtrue[qt], mx2[qt]);
+      }
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) mref[qt] = (mtrue[qt] == -INFINITY) ? 0.0f : mtrue[qt];
+      zero_acc();
+      prologue();
+      run(mref);
+    }
   }
 
   const long long out_base = (long long)b * s.osb + (long long)h * s.osh;
 #pragma unroll
   for (int qt = 0; qt < 4; ++qt) {
-    const float l = l_run[qt];
+    const float l = lacc[qt][0];  // every row of the ones product holds the column sum
     const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
     const int row = a * kBlock + 16 * qt + l16;
     if (row < s.N) {
