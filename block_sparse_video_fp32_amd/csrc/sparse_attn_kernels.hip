@@ -34,6 +34,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "sa_internal.h"
 #include "sparse_attn.h"
@@ -575,12 +576,6 @@ __global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __r
       for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  // Is half tile t an exact tile with every key valid (no per-key term)?
-  auto plain_tile = [&](int t) {
-    if (t >= nexact) return false;
-    const int c = s.dense ? (t >> 1) : list[t >> 1];
-    return c >= 0 && c < nb && (c < nb - 1 || (t & 1) * 32 + 32 <= s.tail);
-  };
   // Row maxima of one half tile's logits (used for the reference only).
   auto row_max = [&](const f32x4 (&st)[4][2], int tt, float (&mx)[4]) {
     float kb[2][4];
@@ -599,8 +594,13 @@ __global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __r
     }
   };
 
-  // Pipeline state: K of the next half tile in kf, V of the current one in
-  // vf, S^T of the current one in the "current" st buffer.
+  // Pipeline state entering step t: S^T of t in the current st buffer, K of
+  // t+1 in kf, V of t in vf.  Step t issues Q K^T of t+1 (MFMA) and the
+  // exponentials of t (VALU) in one basic block, so that the scheduler can
+  // interleave them and the MFMA pipe of this single wave works while the
+  // VALU does; P V of t and the row sums (an MFMA against ones) follow.  K of
+  // t+2 and V of t+1 are requested as soon as their registers are free.
+  // Indices past the end are clamped (a redundant last Q K^T).
   uint4 kf[2][NS], vf[NDT];
   f32x4 stA[4][2], stB[4][2];
   auto prologue = [&]() {
@@ -612,38 +612,26 @@ __global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __r
     tile_ptrs(min(1, T - 1), kb0, vb0);
     load_k<D>(kf, kb0, lane);
   };
-  // One iteration: Q K^T of t+1 is issued first so that the exponentials of
-  // t (VALU) run while it is in the MFMA pipe; then P V of t and the row
-  // sums (an MFMA against ones); K of t+2 and V of t+1 are requested as soon
-  // as their registers are free.  Indices past the end are clamped (a
-  // redundant last Q K^T).
-  auto step = [&](int t, const f32x4 (&st)[4][2], f32x4 (&st_next)[4][2], const float (&mref)[4]) {
+  auto step = [&](auto plain_c, int t, const f32x4 (&st)[4][2], f32x4 (&st_next)[4][2],
+                  const float (&mref)[4]) {
+    constexpr bool plain = decltype(plain_c)::value;
+    const uint16_t *kb2, *vb2, *kb1, *vb1;
+    tile_ptrs(min(t + 2, T - 1), kb2, vb2);
+    tile_ptrs(min(t + 1, T - 1), kb1, vb1);
+    float kb[2][4];
+    if constexpr (!plain) key_bias(t, kb);
     qk(kf, st_next);
-    {
-      const uint16_t *kb2, *vb2;
-      tile_ptrs(min(t + 2, T - 1), kb2, vb2);
-      load_k<D>(kf, kb2, lane);
-    }
+    load_k<D>(kf, kb2, lane);
     bf16x8 pb[4];
-    if (plain_tile(t)) {
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
+    for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pb[qt][kt * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[qt][kt][i], s.c1, -mref[qt]));
-    } else {
-      float kb[2][4];
-      key_bias(t, kb);
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pb[qt][kt * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[qt][kt][i], s.c1, kb[kt][i] - mref[qt]));
-    }
+        for (int i = 0; i < 4; ++i) {
+          const float bias = plain ? -mref[qt] : kb[kt][i] - mref[qt];
+          pb[qt][kt * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[qt][kt][i], s.c1, bias));
+        }
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
 #pragma unroll
@@ -652,17 +640,36 @@ __global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __r
                                                              acc[qt][dt], 0, 0, 0);
       lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qt], lacc[qt], 0, 0, 0);
     }
-    {
-      const uint16_t *kb1, *vb1;
-      tile_ptrs(min(t + 1, T - 1), kb1, vb1);
-      load_v<D>(vf, vb1, lane);
-    }
+    load_v<D>(vf, vb1, lane);
   };
+  // Exact half tiles come first (lists are ascending) and only a ragged
+  // last block and the centroid tiles need per-key terms, so the plain tiles
+  // are a prefix of the sequence and each of the two loops below runs one
+  // step variant.
+  int nplain = nexact;
+  if (nexact > 0 && s.tail < kBlock) {
+    const int clast = s.dense ? nb - 1 : list[count - 1];
+    if (clast == nb - 1) nplain = nexact - 2;
+  }
   auto run = [&](const float (&mref)[4]) {
-    for (int t = 0; t < T; t += 2) {
-      step(t, stA, stB, mref);
-      if (t + 1 < T) step(t + 1, stB, stA, mref);
+    int t = 0;
+    for (; t + 1 < nplain; t += 2) {
+      step(std::true_type{}, t, stA, stB, mref);
+      step(std::true_type{}, t + 1, stB, stA, mref);
     }
+    if (t < nplain) {
+      step(std::true_type{}, t, stA, stB, mref);
+      ++t;
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) stA[qt][kt] = stB[qt][kt];
+    }
+    for (; t + 1 < T; t += 2) {
+      step(std::false_type{}, t, stA, stB, mref);
+      step(std::false_type{}, t + 1, stB, stA, mref);
+    }
+    if (t < T) step(std::false_type{}, t, stA, stB, mref);
   };
 
   float mref[4] = {0.f, 0.f, 0.f, 0.f};
