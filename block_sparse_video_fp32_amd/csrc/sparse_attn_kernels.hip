@@ -543,17 +543,21 @@ __global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __r
         kb[kt][i] = centroid ? (ok_c ? bc : -INFINITY) : (ok_e ? 0.0f : -INFINITY);
       }
   };
+  // Q K^T of one half tile: the d steps are the outer loop so that eight
+  // independent accumulators separate two MFMAs into the same one.
   auto qk = [&](const uint4 (&kf)[2][NS], f32x4 (&st)[4][2]) {
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        st[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < 2; ++kt) st[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ss = 0; ss < NS; ++ss)
+    for (int ss = 0; ss < NS; ++ss)
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
           st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][ss]),
                                                               qf[qt][ss], st[qt][kt], 0, 0, 0);
-      }
   };
 
   // Softmax reference.  Every logit x of query row q is scored as
