@@ -17,7 +17,6 @@ Prints ONE JSON line (rank 0 = the only rank).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -32,12 +31,6 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 
-def _kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "block_sparse_video_fp32_amd", "csrc", "sparse_attn_kernels.hip")
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
 def _traffic(workload: str):
     """HBM bytes per attend launch from the committed rocprofv3 counter runs,
     or None when they are missing or were taken on other kernel source."""
@@ -46,7 +39,9 @@ def _traffic(workload: str):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha256_16") != _kernel_source_hash():
+    from block_sparse_video_fp32_amd.profiling import kernel_source_hash
+
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return d.get("bytes_per_launch")
 
@@ -135,6 +130,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 256 MiB device copy before the steps (scales rocprofv3 byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -162,6 +159,13 @@ def main():
     plan = binding.SparseAttnPlan(B, N, H, D, prefix_len=w.prefix_len, **rkw)
     ws = plan.workspace(dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.copy_calibration:
+        src = torch.empty(128 * 1024 * 1024, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         plan.pool(q, k, v, ws)
