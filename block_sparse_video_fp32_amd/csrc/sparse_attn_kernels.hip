@@ -14,22 +14,27 @@
 //                  ballot compaction into an ascending index list
 //                  (thakicloud accel-stack post, 이 기술은 무엇인가; Spark-H3
 //                  news, 워크플로: topk_ratio).
-//   attend_kernel  one wave per (b, h, query block): exact bf16 attention on
-//                  MFMA over the listed key blocks, then one centroid logit
-//                  per unselected block with the log-mass bias, all merged
-//                  into the same FP32 online softmax (Star7 README, Sol:
-//                  missed blocks contribute through a K/V centroid in the
-//                  same FP32 online softmax).
+//   attend_kernel  one workgroup per pair of neighbouring query blocks of
+//                  one (b, h): exact bf16 attention on MFMA over the key
+//                  blocks either block listed, K and V^T staged in LDS by
+//                  direct global->LDS copies, then one centroid logit per
+//                  unselected block with the log-mass bias, all merged into
+//                  the same FP32 softmax (Star7 README, Sol: missed blocks
+//                  contribute through a K/V centroid in the same FP32 online
+//                  softmax).
 //
-// Packed operand layouts (bf16).  A "half tile" is 32 keys x D.
-//   K half tile:   element ((kt*NS + ss)*64 + lane)*8 + e holds
-//                  K[16 kt + lane%16][32 ss + 8 (lane/16) + e]   (NS = D/32)
-//   V^T half tile: element d*32 + 8 g + e holds V[keyslot(g, e)][d] with
-//                  keyslot(g, e) = 4 g + e for e < 4, 16 + 4 g + e - 4 else.
-// These are the A-operand registers of v_mfma_f32_16x16x32_bf16 for
-// S^T = K Q^T and O^T = V^T P^T; keyslot() is the order in which the S^T
-// accumulator holds the keys, so P^T goes from accumulator to B operand
-// without any lane movement.
+// Packed operand layouts (bf16).  A "half tile" is 32 keys x D, stored as
+// D/16 blocks of 64 lanes x 8 elements (1 KB at D = 128); kappa(r) is r with
+// bits 3 and 4 swapped.
+//   K half tile:   element ((m*64 + l)*8 + e) holds
+//                  K[kappa(l % 32)][16 m + 8 (l / 32) + e]
+//   V^T half tile: element ((m*64 + l)*8 + e), m = 2 dt + j, holds
+//                  V[16 (e / 4) + 8 j + 4 (l / 32) + e % 4][32 dt + l % 32]
+// Block m of K is lane l's A operand of the m-th v_mfma_f32_32x32x16_bf16 of
+// S^T = K Q^T; block m of V^T is the A operand of k-step j of O^T = V^T P^T
+// for d tile dt.  The key order is the one in which the S^T accumulator
+// holds the keys, so P^T goes from accumulator to B operand without any lane
+// movement, and each block is one linear 1 KB copy into LDS.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -137,12 +142,13 @@ __global__ __launch_bounds__(256) void pool_q_kernel(Shape s, const uint16_t* __
   }
 }
 
-// Position of key r (0..31 within a half tile) in the packed V^T order.
-__device__ __forceinline__ int v_slot(int r) {
-  return (r & 16) ? 8 * ((r - 16) >> 2) + 4 + (r & 3) : 8 * (r >> 2) + (r & 3);
+// Packed half-tile orders (see the file header): kappa(r) swaps bits 3 and 4
+// of a key index r (an involution).
+__device__ __forceinline__ int kappa(int r) { return (r & 7) | ((r & 8) << 1) | ((r & 16) >> 1); }
+// Key held in element e of lane l's chunk of a V^T block of k-step j.
+__device__ __forceinline__ int vt_key(int j, int l, int e) {
+  return 16 * (e >> 2) + 8 * j + 4 * (l >> 5) + (e & 3);
 }
-// Key held in packed V^T position 8 g + e.
-__device__ __forceinline__ int v_key(int g, int e) { return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4); }
 
 // ---------------------------------------------------------------------------
 // pack_kv: grid (n_bp, H, B), 256 threads.  Stages the block's K and V rows
@@ -167,16 +173,17 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
   const int J = j >> 5, r = j & 31;  // centroid half tile and row
   uint16_t* kc = ws.kbp + (bh * (s.nbp / 32) + J) * HT;
   uint16_t* vc = ws.vbp + (bh * (s.nbp / 32) + J) * HT;
-  const int ckt = r >> 4, cl16 = r & 15;
-  auto kc_index = [&](int d) {
-    const int ss = d >> 5, g = (d & 31) >> 3, e = d & 7;
-    return ((ckt * NS + ss) * 64 + 16 * g + cl16) * 8 + e;
+  // element of centroid row r, dimension d, in the packed K and V^T orders
+  auto kc_index = [&](int d) { return (((d >> 4) * 64 + kappa(r) + 32 * ((d >> 3) & 1)) * 8) + (d & 7); };
+  auto vc_index = [&](int d) {
+    const int m = 2 * (d >> 5) + ((r >> 3) & 1), l = (d & 31) + 32 * ((r >> 2) & 1);
+    return (m * 64 + l) * 8 + 4 * (r >> 4) + (r & 3);
   };
 
   if (j >= s.nb) {
     if (tid < D) {
       kc[kc_index(tid)] = 0;
-      vc[tid * 32 + v_slot(r)] = 0;
+      vc[vc_index(tid)] = 0;
     }
     return;
   }
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
       kc[kc_index(d)] = (uint16_t)f32_to_bf16_bits(mean);
     } else {
       ws.vbar[(bh * s.nb + j) * D + d] = mean;
-      vc[d * 32 + v_slot(r)] = (uint16_t)f32_to_bf16_bits(mean);
+      vc[vc_index(d)] = (uint16_t)f32_to_bf16_bits(mean);
     }
   }
 
@@ -217,22 +224,21 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
 #pragma unroll
   for (int i = 0; i < CPR / 4; ++i) {
     const int o = tid + 256 * i;  // output 16-byte chunk, 64 * CPR of them
+    const int ht = o / (64 * (D / 16)), m = (o / 64) % (D / 16), l = o % 64;
     {
-      const int ht = o / (128 * NS), rem = o % (128 * NS);
-      const int kt = rem / (64 * NS), rem2 = rem % (64 * NS);
-      const int ss = rem2 / 64, lane = rem2 % 64;
-      const int row = 32 * ht + 16 * kt + (lane & 15);
-      const int d0 = 32 * ss + 8 * (lane >> 4);
+      // K: chunk (m, l) = K[kappa(l % 32)][16 m + 8 (l / 32) .. +8]
+      const int row = 32 * ht + kappa(l & 31);
+      const int d0 = 16 * m + 8 * (l >> 5);
       *reinterpret_cast<uint4*>(kp + (long long)o * 8) = *reinterpret_cast<const uint4*>(Kl + row * LS + d0);
     }
     {
-      const int ht = o / (4 * D), rem = o % (4 * D);
-      const int d = rem >> 2, g = rem & 3;
+      // V^T: chunk (m = 2 dt + jj, l) = V[vt_key(jj, l, e)][32 dt + l % 32], e = 0..7
+      const int d = 32 * (m >> 1) + (l & 31), jj = m & 1;
       uint32_t w[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t lo = Vl[(32 * ht + v_key(g, 2 * e2)) * LS + d];
-        const uint32_t hi = Vl[(32 * ht + v_key(g, 2 * e2 + 1)) * LS + d];
+        const uint32_t lo = Vl[(32 * ht + vt_key(jj, l, 2 * e2)) * LS + d];
+        const uint32_t hi = Vl[(32 * ht + vt_key(jj, l, 2 * e2 + 1)) * LS + d];
         w[e2] = lo | (hi << 16);
       }
       *reinterpret_cast<uint4*>(vp + (long long)o * 8) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -405,327 +411,489 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
 }
 
 // ---------------------------------------------------------------------------
-// attend: one wave per (b, h, query block); grid B*H*n_b in an XCD-aware
-// order.  The wave keeps its 64 query rows as MFMA B operands (Q^T) in
-// registers and walks half tiles of 32 keys: first the two halves of every
-// listed key block, then the centroid half tiles that hold at least one
-// unselected block.  Per half tile:
-//   S^T[key][q] = K Q^T            8 v_mfma_f32_16x16x32_bf16 per 16 queries
-//   online softmax per query       in-lane over 8 keys + 2 cross-lane steps
-//   O^T[d][q] += V^T P^T           8 MFMAs per 16 queries
-// Operands come from the packed buffers in a double-buffered register
-// pipeline (the next half tile is loaded while the current one computes).
+// attend: one workgroup of four waves per pair of neighbouring query blocks
+// (a0 = 2p, a1 = 2p + 1) of one (b, h); wave w owns the 32 query rows
+// 32 (w & 1) .. + 31 of block a0 + (w >> 1).  The pair walks the union of
+// its two key-block lists, in half tiles of 32 keys: first both halves of
+// every key block either block selected (ascending), then every centroid
+// half tile that either block needs.  Each half tile (K and V^T, 16 KB at
+// D = 128) is copied once from global memory straight into an LDS ring of S
+// stages and read from there by the waves whose block needs it; the other
+// waves skip it.  Per half tile and wave (32 keys x 32 queries):
+//   S^T = K Q^T     D/16 v_mfma_f32_32x32x16_bf16
+//   P = exp2(S^T c1 + bias - mref), row sums in-lane (VALU)
+//   O^T += V^T P^T  D/16 MFMAs
+// Two waves run per SIMD, so one wave's exponentials overlap the other's
+// MFMAs.
+//
+// LDS order of a half tile: 1 KB blocks of 64 lanes x 16 bytes, each the
+// A operand of one MFMA for lane = position:
+//   K block s (s < D/16):      lane l holds K[key(l % 32)][16 s + 8 (l/32) .. +8]
+//   V^T block 2 dt + j:        lane l holds V^T[32 dt + l % 32][keys of
+//                              k-step j, 8 (l/32) .. +8]
+// with key(r) = r with bits 3 and 4 swapped: exactly the packed K and V^T
+// half tiles one after the other.  That key order makes the S^T accumulator
+// registers 8 j .. 8 j + 7 of a lane exactly the P^T B operand of k-step j,
+// so P^T goes from accumulator to operand with no lane movement, and every
+// LDS read is a linear, conflict-free ds_read_b128.
 // ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ void load_k(uint4 (&kf)[2][D / 32], const uint16_t* __restrict__ base, int lane) {
-  constexpr int NS = D / 32;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int ss = 0; ss < NS; ++ss)
-      kf[kt][ss] = *reinterpret_cast<const uint4*>(base + ((kt * NS + ss) * 64 + lane) * 8);
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// s_waitcnt immediate: vmcnt(n) and lgkmcnt(0), expcnt untouched.
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Workgroup barrier that orders LDS accesses around it in the compiler but,
+// unlike __syncthreads, does not wait for outstanding global->LDS copies.
+__device__ __forceinline__ void ring_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int D>
-__device__ __forceinline__ void load_v(uint4 (&vf)[D / 16], const uint16_t* __restrict__ base, int lane) {
-  const int l16 = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *reinterpret_cast<const uint4*>(base + (16 * dt + l16) * 32 + 8 * g);
+// Entry of union half tile u of a workgroup: index (key block, or centroid
+// half tile when u >= te) in bits 0..11, flags (which of the two query
+// blocks needs it) above.
+__device__ __forceinline__ int union_entry(const uint16_t* ulist, const uint16_t* uct, int te, int u) {
+  const int e = (u >= te) ? (int)uct[min(max(u - te, 0), SA_MAX_BLOCKS / 32 - 1)]
+                          : (int)ulist[min(u >> 1, SA_MAX_BLOCKS - 1)];
+  return __builtin_amdgcn_readfirstlane(e);
 }
 
-template <int D>
-__global__ __launch_bounds__(64) void attend_kernel(Shape s, const uint16_t* __restrict__ q,
-                                                    uint16_t* __restrict__ out, Workspace ws) {
-  constexpr int NS = D / 32, NDT = D / 16, HT = 32 * D;
-  __shared__ uint32_t selbits[SA_MAX_BLOCKS / 32];
-  __shared__ int ctile[SA_MAX_BLOCKS / 32];
+// This wave's PER 1 KB blocks of one half tile, global -> LDS: lane l's 16
+// bytes land at dst + 1024 i + 16 l.  Written as asm so that the compiler
+// does not track these copies: it would otherwise wait for all of them
+// before every LDS read.  Completion is established by the explicit vmcnt
+// waits and barriers of the ring.  The instruction has no result register.
+template <int PER>
+__device__ __forceinline__ void copy_blocks(const uint16_t* src, const int (&doff)[PER], uint32_t dst) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src + doff[i]), "s"(dst + i * 1024)
+                 : "memory", "m0");
+}
 
-  // Consecutive logical ids go to one XCD (workgroups are dealt to the 8 XCDs
-  // round-robin), so one head's query blocks share that XCD's L2.
+__device__ __forceinline__ bf16x8 lds_frag(const uint8_t* stage, int blk, int lane) {
+  return *reinterpret_cast<const bf16x8*>(stage + blk * 1024 + lane * 16);
+}
+
+// S^T (32 keys x this wave's 32 queries) of the half tile in `stage`.
+template <int NK>
+__device__ __forceinline__ f32x16 tile_qk(const uint8_t* stage, int lane, const bf16x8 (&qf)[NK]) {
+  bf16x8 kf[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) kf[k] = lds_frag(stage, k, lane);
+  f32x16 sacc = {};
+#pragma unroll
+  for (int k = 0; k < NK; ++k) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], sacc, 0, 0, 0);
+  // all LDS reads first, then the MFMA chain
+  __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
+  return sacc;
+}
+
+// Additive per-key term (log2 domain) of a half tile for one query block:
+// 0 for a valid key of an exact block and -inf past N; for a centroid,
+// log2(n_c) (0 without the log-mass bias) if that block exists and the query
+// block did not select it, else -inf.  Register i of the lane holds key
+// key(8 (i/4) + 4 hh + i % 4).
+__device__ __forceinline__ void tile_key_bias(float (&kb)[16], bool cen, int c, int half, int N, int nb,
+                                              uint32_t sbits, int hh, float bias_full, float bias_tail) {
+  const int nvalid = cen ? 0 : min(kBlock, N - c * kBlock);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int kap = 16 * ((i >> 2) & 1) + 8 * (i >> 3) + 4 * hh + (i & 3);
+    const bool ok_e = 32 * half + kap < nvalid;
+    const int cc = 32 * c + kap;
+    const bool ok_c = cc < nb && !((sbits >> kap) & 1u);
+    const float bc = (cc == nb - 1) ? bias_tail : bias_full;
+    kb[i] = cen ? (ok_c ? bc : -INFINITY) : (ok_e ? 0.0f : -INFINITY);
+  }
+}
+
+// Maximum logit of this lane's query over one half tile.
+__device__ __forceinline__ float tile_row_max(const f32x16& sacc, const float (&kb)[16], float c1) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fmaf(sacc[i], c1, kb[i]));
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
+// P = exp2(S^T c1 + kb - mref) in bf16, row sums, O^T += V^T P^T.
+template <int NK, bool PLAIN>
+__device__ __forceinline__ void tile_pv(const uint8_t* stage, int lane, const f32x16& sacc, const float (&kb)[16],
+                                        float c1, float mref, f32x16 (&acc)[NK / 2], float (&lsum)[2]) {
+  bf16x8 vf[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) vf[k] = lds_frag(stage, NK + k, lane);
+  float pe[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pe[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c1, (PLAIN ? 0.0f : kb[i]) - mref));
+  bf16x8 pb[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[j][e] = (__bf16)pe[8 * j + e];
+  // Row sums of the bf16-rounded P that the MFMAs use (so that the final
+  // division is consistent with the accumulated P V), two bf16 per
+  // v_dot2_f32_bf16 against (1, 1), in two independent chains.
+  const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint4 wd = __builtin_bit_cast(uint4, pb[j]);
+    lsum[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd.x), one2, lsum[0], false);
+    lsum[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd.y), one2, lsum[1], false);
+    lsum[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd.z), one2, lsum[0], false);
+    lsum[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd.w), one2, lsum[1], false);
+  }
+#pragma unroll
+  for (int dt = 0; dt < NK / 2; ++dt)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * dt + j], pb[j], acc[dt], 0, 0, 0);
+  // V^T reads are in flight while the exponentials run
+  __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
+}
+
+template <int D, int S>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_kernel(
+    Shape s, const uint16_t* __restrict__ q, uint16_t* __restrict__ out, Workspace ws) {
+  constexpr int NK = D / 16;          // QK k-steps = K blocks = PV MFMAs per tile
+  constexpr int NDT = D / 32;         // 32-row d tiles of O^T
+  constexpr int NBLK = 2 * NK;        // 1 KB LDS blocks per half tile
+  constexpr int PER = NBLK / 4;       // copies per wave per half tile
+  constexpr int HT = 32 * D;          // elements of a half tile
+  constexpr int STAGE = NBLK * 1024;  // bytes of one ring stage
+  constexpr int NW = SA_MAX_BLOCKS / 32;
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // S * STAGE bytes
+  __shared__ uint32_t sel[2][NW];            // selected key blocks of a0, a1
+  __shared__ uint16_t ulist[SA_MAX_BLOCKS];  // union of the two lists
+  __shared__ uint16_t uct[NW];               // centroid half tiles either needs
+  __shared__ int info[8];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7, kx = bid >> 3, qq = G >> 3, rr = G & 7;
   const int lid = (xcd < rr) ? xcd * (qq + 1) + kx : rr * (qq + 1) + (xcd - rr) * qq + kx;
-  const int nb = s.nb;
-  const int a = lid % nb;
-  const int bhi = lid / nb;
+  const int nb = s.nb, N = s.N;
+  const float c1 = s.c1;
+  const int np = (nb + 1) >> 1;
+  const int p = lid % np;
+  const int bhi = lid / np;
   const int h = bhi % s.H, b = bhi / s.H;
   const long long bh = bhi;
-  const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
+  const int a0 = 2 * p;
+  const bool has1 = a0 + 1 < nb;
+  const int x = w >> 1;  // this wave's block is a0 + x
+  const bool exists = x == 0 || has1;
+  const int myflag = 1 << x;
 
-  // Q^T fragments: query a*64 + 16 qt + l16, d = 32 ss + 8 g + e.
-  const long long in_base = (long long)b * s.isb + (long long)h * s.ish;
-  bf16x8 qf[4][NS];
+  // Q^T B-operand fragments: lane l holds Q[row l % 32][16 k + 8 (l/32) .. +8].
+  const int qrow = (a0 + x) * kBlock + 32 * (w & 1) + l32;
+  bf16x8 qf[NK];
+  {
+    const uint16_t* qp = q + (long long)b * s.isb + (long long)h * s.ish + (long long)qrow * s.ist + 8 * hh;
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const int row = a * kBlock + 16 * qt + l16;
-#pragma unroll
-    for (int ss = 0; ss < NS; ++ss) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (row < s.N) x = *reinterpret_cast<const uint4*>(q + in_base + (long long)row * s.ist + 32 * ss + 8 * g);
-      qf[qt][ss] = __builtin_bit_cast(bf16x8, x);
+    for (int k = 0; k < NK; ++k) {
+      uint4 v4 = make_uint4(0, 0, 0, 0);
+      if (exists && qrow < N) v4 = *reinterpret_cast<const uint4*>(qp + 16 * k);
+      qf[k] = __builtin_bit_cast(bf16x8, v4);
     }
   }
 
-  int count = nb;
-  if (!s.dense) count = min(max(ws.counts[bh * nb + a], 0), nb);
-  const int* list = ws.lists + (bh * nb + a) * (long long)nb;
-  const int nct = s.nbp / 32;  // centroid half tiles
-  int nc = 0;                  // centroid half tiles to visit
-  if (!s.dense && s.centroid && count < nb) {
-    for (int i = lane; i < nct; i += 64) selbits[i] = 0u;
+  // Union of the two lists and the centroid half tiles either block needs,
+  // as a table in LDS, and the first half tile each block needs.
+  const int nct = s.nbp / 32;
+  if (s.dense) {
+    const int fl = (1 | ((int)has1 << 1)) << 12;
+    for (int i = tid; i < nb; i += 256) ulist[i] = (uint16_t)(i | fl);
+    if (tid == 0) {
+      info[0] = nb;
+      info[1] = 0;
+      info[3] = 0;
+      info[4] = has1 ? 0 : 2 * nb;
+    }
+  } else {
+    const int cnt0 = min(max(ws.counts[bh * nb + a0], 0), nb);
+    const int cnt1 = has1 ? min(max(ws.counts[bh * nb + a0 + 1], 0), nb) : 0;
+    for (int i = tid; i < 2 * NW; i += 256) sel[i / NW][i % NW] = 0u;
     __syncthreads();
-    for (int i = lane; i < count; i += 64) {
-      const int c = list[i];
-      if (c >= 0 && c < nb) atomicOr(&selbits[c >> 5], 1u << (c & 31));
+    const int* L0 = ws.lists + (bh * nb + a0) * (long long)nb;
+    for (int i = tid; i < cnt0; i += 256) {
+      const int c = L0[i];
+      if (c >= 0 && c < nb) atomicOr(&sel[0][c >> 5], 1u << (c & 31));
+    }
+    for (int i = tid; i < cnt1; i += 256) {
+      const int c = L0[nb + i];
+      if (c >= 0 && c < nb) atomicOr(&sel[1][c >> 5], 1u << (c & 31));
     }
     __syncthreads();
-    // keep the centroid half tiles with at least one unselected, existing block
-    int base = 0;
-    for (int i0 = 0; i0 < nct; i0 += 64) {
-      const int i = i0 + lane;
-      bool keep = false;
-      if (i < nct) {
-        const int valid = min(32, nb - 32 * i);
-        const uint32_t vmask = valid >= 32 ? 0xffffffffu : ((1u << max(valid, 0)) - 1u);
-        keep = (~selbits[i] & vmask) != 0u;
+    if (w == 0) {
+      const int nwords = (nb + 31) >> 5;
+      const uint32_t m0 = lane < nwords ? sel[0][lane] : 0u, m1 = lane < nwords ? sel[1][lane] : 0u;
+      uint32_t um = m0 | m1;
+      const int cw = __popc(um);
+      int incl = cw;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
       }
-      const uint64_t m = __ballot(keep);
-      if (keep) ctile[base + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = i;
-      base += __popcll(m);
-    }
-    nc = base;
-    __syncthreads();
-  }
-  const int T = 2 * count + nc;
-
-  // Half tile t: pointers into the packed buffers and the additive per-key
-  // term in the log2 domain (0 for a valid key of an exact block, log2(n_c)
-  // or 0 for an unselected centroid, -inf for keys past N, selected
-  // centroids and centroid rows past n_b), the same for every query.  Both
-  // are computed without branches so that the loop body stays one block.
-  const uint16_t* kp_bh = ws.kp + bh * nb * 2LL * HT;
-  const uint16_t* vp_bh = ws.vp + bh * nb * 2LL * HT;
-  const uint16_t* kc_bh = ws.kbp + bh * nct * (long long)HT;
-  const uint16_t* vc_bh = ws.vbp + bh * nct * (long long)HT;
-  const int nexact = 2 * count;
-  auto tile_off = [&](int t, bool& centroid, int& c) {
-    centroid = t >= nexact;
-    const int ce = s.dense ? (t >> 1) : list[min(t, nexact - 1) >> 1];
-    const int ci = ctile[max(t - nexact, 0)];
-    c = centroid ? ci : ((ce >= 0 && ce < nb) ? ce : -1);
-    const long long e_off = ((long long)max(c, 0) * 2 + (t & 1)) * HT;
-    const long long c_off = (long long)ci * HT;
-    return centroid ? c_off : e_off;
-  };
-  auto tile_ptrs = [&](int t, const uint16_t*& kb, const uint16_t*& vb) {
-    bool centroid;
-    int c;
-    const long long off = tile_off(t, centroid, c);
-    kb = (centroid ? kc_bh : kp_bh) + off;
-    vb = (centroid ? vc_bh : vp_bh) + off;
-  };
-  auto key_bias = [&](int t, float (&kb)[2][4]) {
-    bool centroid;
-    int c;
-    tile_off(t, centroid, c);
-    // exact: valid keys 32*(t&1) + r < nvalid; centroid: r unselected and 32c + r < nb
-    const int nvalid = (c >= 0) ? min(kBlock, s.N - c * kBlock) : 0;
-    const uint32_t sel = centroid ? selbits[c] : 0u;
+      const int excl = incl - cw;
+      // union position of the first block of each list
+      int first[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * kt + 4 * g + i;
-        const int cc = 32 * c + r;
-        const bool ok_e = 32 * (t & 1) + r < nvalid;
-        const bool ok_c = cc < nb && !((sel >> r) & 1u);
-        const float bc = (cc == nb - 1) ? s.bias_tail : s.bias_full;
-        kb[kt][i] = centroid ? (ok_c ? bc : -INFINITY) : (ok_e ? 0.0f : -INFINITY);
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t mk = k ? m1 : m0;
+        const uint64_t any = __ballot(mk != 0u);
+        const int fl = any ? __ffsll((long long)any) - 1 : 0;
+        const int pos = excl + __popc(um & ((mk & (0u - mk)) - 1u));
+        first[k] = any ? 2 * __shfl(pos, fl) : -1;
       }
-  };
-  // Q K^T of one half tile: the d steps are the outer loop so that eight
-  // independent accumulators separate two MFMAs into the same one.
-  auto qk = [&](const uint4 (&kf)[2][NS], f32x4 (&st)[4][2]) {
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) st[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ss = 0; ss < NS; ++ss)
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][ss]),
-                                                              qf[qt][ss], st[qt][kt], 0, 0, 0);
-  };
-
-  // Softmax reference.  Every logit x of query row q is scored as
-  // p = exp2(x - mref[q]) with a fixed mref[q]: the exact maximum over the
-  // row's first half tile plus 32 (log2 units).  Terms of that tile then lie
-  // below 2^-32 and the row's largest term is at least 2^-32, far inside the
-  // fp32 / bf16 exponent range, and no running maximum or rescaling of the
-  // accumulators is needed.  The ratio acc / l is independent of mref, so
-  // this is the same softmax up to rounding.  Should a later term exceed
-  // mref by so much that the row sum leaves [0, 2^100] (or is not finite),
-  // the query block is recomputed with the exact row maxima from a
-  // Q K^T-only pass.
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
-  f32x4 acc[4][NDT], lacc[4];
-  auto zero_acc = [&]() {
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  // Row maxima of one half tile's logits (used for the reference only).
-  auto row_max = [&](const f32x4 (&st)[4][2], int tt, float (&mx)[4]) {
-    float kb[2][4];
-    key_bias(tt, kb);
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaf(st[qt][kt][i], s.c1, kb[kt][i]));
-      const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-      m = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
-      const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-      mx[qt] = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
-    }
-  };
-
-  // Pipeline state entering step t: S^T of t in the current st buffer, K of
-  // t+1 in kf, V of t in vf.  Step t issues Q K^T of t+1 (MFMA) and the
-  // exponentials of t (VALU) in one basic block, so that the scheduler can
-  // interleave them and the MFMA pipe of this single wave works while the
-  // VALU does; P V of t and the row sums (an MFMA against ones) follow.  K of
-  // t+2 and V of t+1 are requested as soon as their registers are free.
-  // Indices past the end are clamped (a redundant last Q K^T).
-  uint4 kf[2][NS], vf[NDT];
-  f32x4 stA[4][2], stB[4][2];
-  auto prologue = [&]() {
-    const uint16_t *kb0, *vb0;
-    tile_ptrs(0, kb0, vb0);
-    load_k<D>(kf, kb0, lane);
-    load_v<D>(vf, vb0, lane);
-    qk(kf, stA);
-    tile_ptrs(min(1, T - 1), kb0, vb0);
-    load_k<D>(kf, kb0, lane);
-  };
-  auto step = [&](auto plain_c, int t, const f32x4 (&st)[4][2], f32x4 (&st_next)[4][2],
-                  const float (&mref)[4]) {
-    constexpr bool plain = decltype(plain_c)::value;
-    const uint16_t *kb2, *vb2, *kb1, *vb1;
-    tile_ptrs(min(t + 2, T - 1), kb2, vb2);
-    tile_ptrs(min(t + 1, T - 1), kb1, vb1);
-    float kb[2][4];
-    if constexpr (!plain) key_bias(t, kb);
-    qk(kf, st_next);
-    load_k<D>(kf, kb2, lane);
-    bf16x8 pb[4];
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float bias = plain ? -mref[qt] : kb[kt][i] - mref[qt];
-          pb[qt][kt * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[qt][kt][i], s.c1, bias));
+      int pos = excl;
+      while (um) {
+        const int bit = __ffs(um) - 1;
+        um &= um - 1u;
+        ulist[pos++] = (uint16_t)((lane * 32 + bit) | (((m0 >> bit) & 1u) << 12) | (((m1 >> bit) & 1u) << 13));
+      }
+      const int nu = __shfl(incl, 63);
+      int ncu = 0;
+      if (s.centroid) {
+        bool n0 = false, n1 = false;
+        if (lane < nct) {
+          const int valid = min(32, nb - 32 * lane);
+          const uint32_t vmask = valid >= 32 ? 0xffffffffu : ((1u << max(valid, 0)) - 1u);
+          n0 = cnt0 < nb && (~m0 & vmask) != 0u;
+          n1 = has1 && cnt1 < nb && (~m1 & vmask) != 0u;
         }
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]), pb[qt],
-                                                             acc[qt][dt], 0, 0, 0);
-      lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qt], lacc[qt], 0, 0, 0);
+        const bool keep = n0 || n1;
+        const uint64_t bm = __ballot(keep);
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const int slot = __popcll(bm & lt);
+        if (keep) uct[slot] = (uint16_t)(lane | ((int)n0 << 12) | ((int)n1 << 13));
+        ncu = __popcll(bm);
+        const uint64_t b0 = __ballot(n0), b1 = __ballot(n1);
+        if (first[0] < 0 && b0) first[0] = 2 * nu + __popcll(bm & ((b0 & (0ull - b0)) - 1ull));
+        if (first[1] < 0 && b1) first[1] = 2 * nu + __popcll(bm & ((b1 & (0ull - b1)) - 1ull));
+      }
+      if (lane == 0) {
+        info[0] = nu;
+        info[1] = ncu;
+        info[3] = first[0] < 0 ? 2 * nu + ncu : first[0];
+        info[4] = first[1] < 0 ? 2 * nu + ncu : first[1];
+      }
     }
-    load_v<D>(vf, vb1, lane);
-  };
-  // Exact half tiles come first (lists are ascending) and only a ragged
+  }
+  if (tid == 0) info[2] = 0;
+  __syncthreads();
+  const int nu = __builtin_amdgcn_readfirstlane(info[0]), ncu = __builtin_amdgcn_readfirstlane(info[1]);
+  const int TE = 2 * nu, TU = TE + ncu;
+  const int fme = __builtin_amdgcn_readfirstlane(info[3 + x]);  // first half tile this wave needs
+
+  // Per-lane element offsets of this wave's copies inside a packed half tile:
+  // waves 0, 1 copy the K blocks, waves 2, 3 the V^T blocks.
+  const bool kwave = w < 2;
+  // (the packed tiles are stored in LDS order: each block is a linear copy)
+  int doff[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) doff[i] = (((w & 1) * PER + i) * 64 + lane) * 8;
+  const uint16_t* ex_bh = (kwave ? ws.kp : ws.vp) + bh * nb * 2LL * HT;
+  const uint16_t* ce_bh = (kwave ? ws.kbp : ws.vbp) + bh * nct * (long long)HT;
+  const uint32_t my_dst =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring + w * PER * 1024;
+  const uint8_t* const rd = ring;
+  const float bias_full = s.bias_full, bias_tail = s.bias_tail;
+
+  // Exact half tiles come first (the union is ascending) and only a ragged
   // last block and the centroid tiles need per-key terms, so the plain tiles
-  // are a prefix of the sequence and each of the two loops below runs one
-  // step variant.
-  int nplain = nexact;
-  if (nexact > 0 && s.tail < kBlock) {
-    const int clast = s.dense ? nb - 1 : list[count - 1];
-    if (clast == nb - 1) nplain = nexact - 2;
-  }
-  auto run = [&](const float (&mref)[4]) {
-    int t = 0;
-    for (; t + 1 < nplain; t += 2) {
-      step(std::true_type{}, t, stA, stB, mref);
-      step(std::true_type{}, t + 1, stB, stA, mref);
-    }
-    if (t < nplain) {
-      step(std::true_type{}, t, stA, stB, mref);
-      ++t;
+  // are a prefix of the sequence.
+  int nplain = TE;
+  if (nu > 0 && s.tail < kBlock && (union_entry(ulist, uct, TE, TE - 1) & 0xfff) == nb - 1) nplain = TE - 2;
+
+  // Softmax reference: every logit x of a query is scored as
+  // p = exp2(x - mref) with a fixed mref, the exact maximum over the first
+  // half tile the query sees plus 32 (log2 units).  Terms of that tile lie
+  // below 2^-32 and the row's largest term is at least 2^-32, well inside
+  // the fp32 / bf16 range, so no running maximum or rescaling is needed; the
+  // ratio acc / l does not depend on mref.  If a later term exceeds mref by
+  // so much that a row sum leaves [0, 2^100] (or is not finite), the pair is
+  // recomputed with the exact row maxima from a Q K^T-only pass.
+  f32x16 acc[NDT];
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
+  float lsum[2] = {0.0f, 0.0f}, mref = 0.0f, mmax = -INFINITY;
+  bool safe = false;
+
+  // One pass over the union through the ring: at step u every wave waits for
+  // its own copies of half tile u, the barrier makes all of them visible and
+  // frees the stage read at step u - 1, and half tile u + S - 1 (clamped to
+  // the last one, so that every step waits on the same count) is requested
+  // into that stage.  Half tile v always lands in stage v % S.  eq[] holds
+  // the table entries of the half tiles in flight (u .. u + S - 2).
+  int eq[S - 1];
+  int st = 0;
+  // Table entries of 64 consecutive half tiles, one per lane, so that a
+  // lookup is a v_readlane instead of an LDS round trip on every step.
+  int tab_base = 0, tabv = 0;
+  auto tab_load = [&](int base) {
+    tab_base = base;
+    const int v = min(base + lane, max(TU - 1, 0));
+    tabv = (v >= TE) ? (int)uct[min(max(v - TE, 0), NW - 1)] : (int)ulist[min(v >> 1, SA_MAX_BLOCKS - 1)];
+  };
+  auto lookup = [&](int v) {
+    if (v >= tab_base + 64) tab_load(v & ~63);
+    return __builtin_amdgcn_readlane(tabv, v - tab_base);
+  };
+  auto copy_tile = [&](int v, int e, int stg) {
+    const int c = e & 0xfff;
+    const long long off = (v >= TE) ? (long long)c * HT : ((long long)c * 2 + (v & 1)) * HT;
+    copy_blocks<PER>(((v >= TE) ? ce_bh : ex_bh) + off, doff, my_dst + stg * STAGE);
+  };
+  auto ring_start = [&]() {
+    st = 0;
+    tab_load(0);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) stA[qt][kt] = stB[qt][kt];
+    for (int k = 0; k < S - 1; ++k) {
+      const int v = min(k, TU - 1);
+      eq[k] = lookup(v);
+      copy_tile(v, eq[k], k);
     }
-    for (; t + 1 < T; t += 2) {
-      step(std::false_type{}, t, stA, stB, mref);
-      step(std::false_type{}, t + 1, stB, stA, mref);
-    }
-    if (t < T) step(std::false_type{}, t, stA, stB, mref);
+  };
+  // Returns the entry of half tile u; afterwards the stage of u is rd + st*STAGE.
+  auto ring_step = [&](int u) {
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 2) * PER));
+    ring_barrier();
+    const int v = min(u + S - 1, TU - 1);
+    const int ev = lookup(v);
+    copy_tile(v, ev, st == 0 ? S - 1 : st - 1);
+    const int eu = eq[0];
+#pragma unroll
+    for (int k = 0; k < S - 2; ++k) eq[k] = eq[k + 1];
+    eq[S - 2] = ev;
+    return eu;
+  };
+  auto ring_next = [&]() { st = (st == S - 1) ? 0 : st + 1; };
+  auto bias_of = [&](int u, int eu, float (&kb)[16]) {
+    const bool cen = u >= TE;
+    tile_key_bias(kb, cen, eu & 0xfff, u & 1, N, nb, sel[x][cen ? (eu & (NW - 1)) : 0], hh, bias_full, bias_tail);
   };
 
-  float mref[4] = {0.f, 0.f, 0.f, 0.f};
-  zero_acc();
-  if (T > 0) {
-    prologue();
-    float mx[4];
-    row_max(stA, 0, mx);
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) mref[qt] = (mx[qt] == -INFINITY) ? 0.0f : mx[qt] + 32.0f;
-    run(mref);
-    bool bad = false;
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) bad |= !(lacc[qt][0] <= 0x1p100f);
-    if (__ballot(bad)) {
-      // Exact row maxima over every half tile, then the same computation.
-      float mtrue[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      for (int t = 0; t < T; ++t) {
-        const uint16_t *kb0, *vb0;
-        tile_ptrs(t, kb0, vb0);
-        load_k<D>(kf, kb0, lane);
-        qk(kf, stA);
-        float mx2[4];
-        row_max(stA, t, mx2);
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) mtrue[qt] = fmaxf(mtrue[qt], mx2[qt]);
+  // Q and the lists are in registers / LDS before the first copy is issued.
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  for (int attempt = 0; attempt < 2 && TU > 0; ++attempt) {
+    if (attempt == 1) {
+      // Safe mode: exact row maxima over every half tile first.
+      ring_start();
+      for (int u = 0; u < TU; ++u) {
+        const int eu = ring_step(u);
+        if ((eu >> 12) & myflag) {
+          const f32x16 sacc = tile_qk<NK>(rd + st * STAGE, lane, qf);
+          float kb[16];
+          bias_of(u, eu, kb);
+          mmax = fmaxf(mmax, tile_row_max(sacc, kb, c1));
+        }
+        ring_next();
       }
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+      mref = (mmax == -INFINITY) ? 0.0f : mmax;
+      lsum[0] = lsum[1] = 0.0f;
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) mref[qt] = (mtrue[qt] == -INFINITY) ? 0.0f : mtrue[qt];
-      zero_acc();
-      prologue();
-      run(mref);
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
+      __syncthreads();
     }
+    ring_start();
+    int u = 0;
+    // half tiles before the first one this wave needs: ring only
+    for (; u < fme; ++u) {
+      ring_step(u);
+      ring_next();
+    }
+    if (u < TU) {
+      const int eu = ring_step(u);
+      const uint8_t* stage = rd + st * STAGE;
+      const f32x16 sacc = tile_qk<NK>(stage, lane, qf);
+      float kb[16];
+      bias_of(u, eu, kb);
+      if (!safe) {
+        const float m = tile_row_max(sacc, kb, c1);
+        mref = (m == -INFINITY) ? 0.0f : m + 32.0f;
+      }
+      tile_pv<NK, false>(stage, lane, sacc, kb, c1, mref, acc, lsum);
+      ring_next();
+      ++u;
+    }
+    for (; u < nplain; ++u) {
+      const int eu = ring_step(u);
+      if ((eu >> 12) & myflag) {
+        const uint8_t* stage = rd + st * STAGE;
+        const f32x16 sacc = tile_qk<NK>(stage, lane, qf);
+        float kb[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kb[i] = 0.0f;
+        tile_pv<NK, true>(stage, lane, sacc, kb, c1, mref, acc, lsum);
+      }
+      ring_next();
+    }
+    for (; u < TU; ++u) {
+      const int eu = ring_step(u);
+      if ((eu >> 12) & myflag) {
+        const uint8_t* stage = rd + st * STAGE;
+        const f32x16 sacc = tile_qk<NK>(stage, lane, qf);
+        float kb[16];
+        bias_of(u, eu, kb);
+        tile_pv<NK, false>(stage, lane, sacc, kb, c1, mref, acc, lsum);
+      }
+      ring_next();
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    if (attempt == 1) break;
+    const float lpart = lsum[0] + lsum[1];
+    const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart), __float_as_uint(lpart), false, false);
+    const float ltot = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
+    if (__ballot(!(ltot <= 0x1p100f)) && lane == 0) info[2] = 1;
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(info[2])) break;
+    safe = true;
   }
 
-  const long long out_base = (long long)b * s.osb + (long long)h * s.osh;
+  const float lpart = lsum[0] + lsum[1];
+  const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart), __float_as_uint(lpart), false, false);
+  const float l = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
+  const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+  if (exists && qrow < N) {
+    uint16_t* o = out + (long long)b * s.osb + (long long)h * s.osh + (long long)qrow * s.ost + 4 * hh;
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const float l = lacc[qt][0];  // every row of the ones product holds the column sum
-    const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
-    const int row = a * kBlock + 16 * qt + l16;
-    if (row < s.N) {
-      uint16_t* o = out + out_base + (long long)row * s.ost;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
+      for (int j = 0; j < 4; ++j) {
         uint2 w2;
-        w2.x = f32_to_bf16_bits(acc[qt][dt][0] * inv) | (f32_to_bf16_bits(acc[qt][dt][1] * inv) << 16);
-        w2.y = f32_to_bf16_bits(acc[qt][dt][2] * inv) | (f32_to_bf16_bits(acc[qt][dt][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(o + 16 * dt + 4 * g) = w2;
+        w2.x = f32_to_bf16_bits(acc[dt][4 * j] * inv) | (f32_to_bf16_bits(acc[dt][4 * j + 1] * inv) << 16);
+        w2.y = f32_to_bf16_bits(acc[dt][4 * j + 2] * inv) | (f32_to_bf16_bits(acc[dt][4 * j + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(o + 32 * dt + 8 * j) = w2;
       }
-    }
   }
+}
+
+// Ring depth: half tile u + 2 is requested while u is computed.  Measured
+// at N = 16384 and 32768, 2, 3 and 4 stages run within 1% of each other.
+constexpr int kAttendStages = 3;
+
+template <int D, int S>
+hipError_t launch_attend_t(const Shape& s, const uint16_t* q, uint16_t* out, const Workspace& ws,
+                           hipStream_t stream) {
+  constexpr int bytes = S * (D / 8) * 1024;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, S>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  dim3 grid((unsigned)((long long)s.B * s.H * ((s.nb + 1) / 2)));
+  hipLaunchKernelGGL((attend_kernel<D, S>), grid, dim3(256), bytes, stream, s, q, out, ws);
+  return hipGetLastError();
 }
 
 template <int D, int R>
@@ -770,15 +938,12 @@ hipError_t launch_select(const Shape& s, const Workspace& ws, hipStream_t stream
   return big ? launch_select_t<64, 8>(s, ws, stream) : launch_select_t<64, 16>(s, ws, stream);
 }
 
+
 hipError_t launch_attend(const Shape& s, const void* q, void* out, const Workspace& ws, hipStream_t stream) {
-  dim3 grid((unsigned)((long long)s.B * s.H * s.nb));
   const auto* qq = static_cast<const uint16_t*>(q);
   auto* oo = static_cast<uint16_t*>(out);
-  if (s.D == 128)
-    hipLaunchKernelGGL(attend_kernel<128>, grid, dim3(64), 0, stream, s, qq, oo, ws);
-  else
-    hipLaunchKernelGGL(attend_kernel<64>, grid, dim3(64), 0, stream, s, qq, oo, ws);
-  return hipGetLastError();
+  if (s.D == 128) return launch_attend_t<128, kAttendStages>(s, qq, oo, ws, stream);
+  return launch_attend_t<64, kAttendStages>(s, qq, oo, ws, stream);
 }
 
 }  // namespace sa

@@ -96,12 +96,12 @@ typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
  *   k_packed          bf16, one 64*D-element tile per (b, h, block): the
  *                     block's K rows (zero past N) in MFMA operand order,
  *                     as two 32-row half tiles; in a half tile, element
- *                     ((kt*NS + ss)*64 + lane)*8 + e holds
- *                     K[16 kt + lane%16][32 ss + 8 (lane/16) + e], NS = D/32.
+ *                     ((m*64 + l)*8 + e) holds
+ *                     K[kappa(l % 32)][16 m + 8 (l / 32) + e], m < D/16,
+ *                     where kappa(r) is r with bits 3 and 4 swapped.
  *   v_packed          bf16, same tiling for V^T: in a half tile, element
- *                     d*32 + 8 g + e holds V[key(g, e)][d], where
- *                     key(g, e) = 4 g + e for e < 4 and 16 + 4 g + e - 4
- *                     otherwise.
+ *                     ((m*64 + l)*8 + e) with m = 2 dt + j holds
+ *                     V[16 (e/4) + 8 j + 4 (l/32) + e % 4][32 dt + l % 32].
  *   kbar_packed,      bf16 centroids (the means rounded to nearest even),
  *   vbar_packed       [B, H, n_bp/32] half tiles in the same two orders;
  *                     block c is row c % 32 of half tile c / 32; rows of
@@ -157,10 +157,11 @@ int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, 
 
 /* Step 4 alone: exact attention over each query block's list and centroid
  * terms for every other block, reading q and, from ws, the packed tiles,
- * counts and lists.  A caller may write its own lists: entries must be
- * distinct block indices in [0, n_b) (out-of-range entries are treated as
- * block 0 with no valid key), counts in [0, n_b]; a query block whose count
- * is n_b gets no centroid term.  On the dense path lists are not read. */
+ * counts and lists.  A caller may write its own lists: entries should be
+ * distinct block indices in [0, n_b) (out-of-range entries are ignored and
+ * a repeated entry counts once), counts in [0, n_b]; a query block whose
+ * count is n_b gets no centroid term.  On the dense path lists are not
+ * read. */
 int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, void* out, void* ws, size_t ws_bytes,
                        void* stream);
 

@@ -137,19 +137,32 @@ def full_parity(q, k, v, **kw):
 # ----------------------------------------------------------------- pooling
 
 
+def _kappa(r):
+    return (r & 7) | ((r & 8) << 1) | ((r & 16) >> 1)
+
+
 def _unpack_k(tile, D):
-    """Packed K half tile (32*D,) -> [32, D] per the order in sparse_attn.h."""
-    NS = D // 32
-    t = tile.reshape(2, NS, 4, 16, 8)  # [kt, ss, g, l16, e]
-    return t.transpose(0, 3, 1, 2, 4).reshape(32, D)  # row 16 kt + l16, col 32 ss + 8 g + e
+    """Packed K half tile (32*D,) -> [32, D] per the order in sparse_attn.h:
+    element ((m*64 + l)*8 + e) is K[kappa(l % 32)][16 m + 8 (l // 32) + e]."""
+    t = tile.reshape(D // 16, 2, 32, 8)  # [m, l // 32, l % 32, e]
+    k = np.empty((32, D), dtype=tile.dtype)
+    for r in range(32):
+        k[_kappa(r)] = t[:, :, r, :].reshape(D)  # d = 16 m + 8 (l // 32) + e
+    return k
 
 
 def _unpack_vt(tile, D):
-    """Packed V^T half tile (32*D,) -> V [32 keys, D]."""
-    t = tile.reshape(D, 4, 8)  # [d, g, e]
-    keys = np.array([[4 * g + e if e < 4 else 16 + 4 * g + e - 4 for e in range(8)] for g in range(4)])
+    """Packed V^T half tile (32*D,) -> V [32 keys, D]: element
+    ((m*64 + l)*8 + e), m = 2 dt + j, is
+    V[16 (e // 4) + 8 j + 4 (l // 32) + e % 4][32 dt + l % 32]."""
+    t = tile.reshape(D // 32, 2, 2, 32, 2, 4)  # [dt, j, l // 32, l % 32, e // 4, e % 4]
     v = np.empty((32, D), dtype=tile.dtype)
-    v[keys.reshape(-1)] = t.reshape(D, 32).T
+    for dt in range(D // 32):
+        for j in range(2):
+            for hh in range(2):
+                for e4 in range(2):
+                    for e0 in range(4):
+                        v[16 * e4 + 8 * j + 4 * hh + e0, 32 * dt : 32 * dt + 32] = t[dt, j, hh, :, e4, e0]
     return v
 
 
@@ -219,6 +232,27 @@ def _small_inputs(shape, seed):
 def test_small_full_parity(name, shape, kw):
     q, k, v = _small_inputs(shape, seed=len(name))
     full_parity(q, k, v, **kw)
+
+
+def _spike_inputs(N, H, D, spike_block, seed):
+    """Every query row and every key of one block lie along the same +-4
+    vector u, so that block's logits (about 16 D * scale) exceed those of the
+    first block a query sees by far more than the 2^100 headroom of the fixed
+    softmax reference: the kernel must take its exact-maximum recompute."""
+    rng = np.random.default_rng(seed)
+    u = np.where(rng.random((1, 1, H, D)) < 0.5, -4.0, 4.0)
+    q = u + 0.5 * rng.standard_normal((1, N, H, D))
+    k = rng.standard_normal((1, N, H, D))
+    v = rng.standard_normal((1, N, H, D))
+    k[:, spike_block * 64 : (spike_block + 1) * 64] = u
+    return tuple(inputs.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("tau", [1.0, -math.inf], ids=["tau1", "dense"])
+def test_logit_spike_recompute(D, tau):
+    q, k, v = _spike_inputs(N=650, H=2, D=D, spike_block=5, seed=D)
+    full_parity(q, k, v, tau=tau)
 
 
 def test_tiny_matches_oracle_lists_exactly():
