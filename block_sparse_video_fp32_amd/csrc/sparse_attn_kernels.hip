@@ -160,7 +160,6 @@ __device__ __forceinline__ int vt_key(int j, int l, int e) {
 template <int D>
 __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v, Workspace ws) {
-  constexpr int NS = D / 32;
   constexpr int CPR = D / 8;
   constexpr int LS = D + 8;  // LDS row stride (bf16)
   constexpr int HT = 32 * D; // elements of one packed half tile
@@ -247,9 +246,10 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
 }
 
 // ---------------------------------------------------------------------------
-// select: grid (ceil(n_b / R), H, B), 256 threads, dynamic LDS.
-// Phase 1: S[r][c] for R query blocks and every key block, fp32, the dot
-// product summed in d order.  Phase 2: wave w routes rows w*R/4 .. +R/4-1.
+// select: grid (ceil(n_b / 16), H, B), 256 threads, dynamic LDS.
+// Phase 1: S[r][c] = Qbar_(a0+r) . Kbar_c for 16 query blocks and every key
+// block, an fp32 GEMM on v_mfma_f32_16x16x4_f32.  Phase 2: wave w routes rows
+// 4w .. 4w + 3.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float f) {
   if (f == 0.0f) f = 0.0f;  // -0 and +0 rank together
@@ -257,14 +257,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int D, int R>
+template <int D>
 __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
-  constexpr int KSTR = D + 4;  // fp32 row stride of the key tile
-  constexpr int RPW = R / 4;   // rows per wave
+  constexpr int R = 16;       // query blocks per workgroup = MFMA rows
+  constexpr int RPW = R / 4;  // rows routed per wave
+  constexpr int KS = D / 4;   // k-steps of the score GEMM
   extern __shared__ __attribute__((aligned(16))) float sm[];
-  float* qs = sm;                 // [R][D]
-  float* ks = qs + R * D;         // [64][KSTR]
-  float* S = ks + 64 * KSTR;      // [R][nb]
+  float* S = sm;                                     // [R][nb]
   int* hist = reinterpret_cast<int*>(S + R * s.nb);  // [4][256]
 
   const int nb = s.nb;
@@ -272,44 +271,55 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
   const int h = blockIdx.y, b = blockIdx.z;
   const long long bh = (long long)b * s.H + h;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, g = lane >> 4;
   const float* qbar = ws.qbar + bh * nb * D;
   const float* kbar = ws.kbar + bh * nb * D;
 
-  for (int i = tid; i < R * D / 4; i += 256) {
-    const int r = i / (D / 4), c4 = i % (D / 4);
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (a0 + r < nb) x = reinterpret_cast<const float4*>(qbar + (long long)(a0 + r) * D)[c4];
-    reinterpret_cast<float4*>(qs + r * D)[c4] = x;
-  }
-  for (int c0 = 0; c0 < nb; c0 += 64) {
-    __syncthreads();
-    for (int i = tid; i < 64 * D / 4; i += 256) {
-      const int r = i / (D / 4), c4 = i % (D / 4);
+  // MFMA operands: lane l holds A = Qbar[a0 + l%16][KS (l/16) + j] and
+  // B = Kbar[c + l%16][KS (l/16) + j] for k-step j, so every k-step sums
+  // four d values and the steps together cover d once (the summation order
+  // differs from a sequential one only by fp32 rounding).
+  float qa[KS];
+  {
+    const int r = a0 + l16;
+#pragma unroll
+    for (int j = 0; j < KS; j += 4) {
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c0 + r < nb) x = reinterpret_cast<const float4*>(kbar + (long long)(c0 + r) * D)[c4];
-      reinterpret_cast<float4*>(ks + r * KSTR)[c4] = x;
+      if (r < nb) x = *reinterpret_cast<const float4*>(qbar + (long long)r * D + KS * g + j);
+      qa[j] = x.x;
+      qa[j + 1] = x.y;
+      qa[j + 2] = x.z;
+      qa[j + 3] = x.w;
     }
-    __syncthreads();
-    float acc[RPW];
+  }
+  auto load_kb = [&](int c, float (&kb)[KS]) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) acc[i] = 0.0f;
-    const float* kr = ks + lane * KSTR;
-#pragma unroll 4
-    for (int d = 0; d < D; d += 4) {
-      const float4 kv = *reinterpret_cast<const float4*>(kr + d);
-#pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const float4 qv = *reinterpret_cast<const float4*>(qs + (w * RPW + i) * D + d);
-        acc[i] = fmaf(qv.x, kv.x, acc[i]);
-        acc[i] = fmaf(qv.y, kv.y, acc[i]);
-        acc[i] = fmaf(qv.z, kv.z, acc[i]);
-        acc[i] = fmaf(qv.w, kv.w, acc[i]);
-      }
+    for (int j = 0; j < KS; j += 4) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < nb) x = *reinterpret_cast<const float4*>(kbar + (long long)c * D + KS * g + j);
+      kb[j] = x.x;
+      kb[j + 1] = x.y;
+      kb[j + 2] = x.z;
+      kb[j + 3] = x.w;
     }
-    const int c = c0 + lane;
-    if (c < nb) {
+  };
+  // Wave w takes the key tiles of 16 blocks at 32 w + 128 t and 32 w + 128 t + 16
+  // (two independent accumulator chains).
+  for (int c0 = 32 * w; c0 < nb; c0 += 128) {
+    float kb0[KS], kb1[KS];
+    load_kb(c0 + l16, kb0);
+    load_kb(c0 + 16 + l16, kb1);
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) S[(w * RPW + i) * nb + c] = acc[i];
+    for (int j = 0; j < KS; ++j) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j], kb0[j], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j], kb1[j], acc1, 0, 0, 0);
+    }
+    // accumulator lane l, register i: row 4 (l/16) + i, key c + l%16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (c0 + l16 < nb) S[(4 * g + i) * nb + c0 + l16] = acc0[i];
+      if (c0 + 16 + l16 < nb) S[(4 * g + i) * nb + c0 + 16 + l16] = acc1[i];
     }
   }
   __syncthreads();
@@ -461,18 +471,28 @@ __device__ __forceinline__ int union_entry(const uint16_t* ulist, const uint16_t
 }
 
 // This wave's PER 1 KB blocks of one half tile, global -> LDS: lane l's 16
-// bytes land at dst + 1024 i + 16 l.  Written as asm so that the compiler
-// does not track these copies: it would otherwise wait for all of them
-// before every LDS read.  Completion is established by the explicit vmcnt
-// waits and barriers of the ring.  The instruction has no result register.
+// bytes land at dst + 1024 i + 16 l (global_load_lds_dwordx4, LDS address in
+// M0).  Written as asm so that the compiler does not track these copies: it
+// would otherwise wait for all of them before every LDS read.  Completion is
+// established by the explicit vmcnt waits and barriers of the ring.  The
+// instruction has no result register.  M0 is saved and restored around each
+// copy (it is reserved to the compiler), with one wait state between the M0
+// write and the copy that reads it.
 template <int PER>
 __device__ __forceinline__ void copy_blocks(const uint16_t* src, const int (&doff)[PER], uint32_t dst) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src + doff[i]), "s"(dst + i * 1024)
-                 : "memory", "m0");
+  for (int i = 0; i < PER; ++i) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src + doff[i]), "s"(dst + i * 1024)
+        : "memory");
+  }
 }
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* stage, int blk, int lane) {
@@ -896,14 +916,14 @@ hipError_t launch_attend_t(const Shape& s, const uint16_t* q, uint16_t* out, con
   return hipGetLastError();
 }
 
-template <int D, int R>
+template <int D>
 hipError_t launch_select_t(const Shape& s, const Workspace& ws, hipStream_t stream) {
-  const size_t lds = (size_t)(R * D + 64 * (D + 4) + R * s.nb) * sizeof(float) + 4 * 256 * sizeof(int);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<D, R>),
+  const size_t lds = (size_t)16 * s.nb * sizeof(float) + 4 * 256 * sizeof(int);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<D>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  dim3 grid((s.nb + R - 1) / R, s.H, s.B);
-  hipLaunchKernelGGL((select_kernel<D, R>), grid, dim3(256), lds, stream, s, ws);
+  dim3 grid((s.nb + 15) / 16, s.H, s.B);
+  hipLaunchKernelGGL((select_kernel<D>), grid, dim3(256), lds, stream, s, ws);
   return hipGetLastError();
 }
 
@@ -933,9 +953,8 @@ hipError_t launch_pack_kv(const Shape& s, const void* k, const void* v, const Wo
 }
 
 hipError_t launch_select(const Shape& s, const Workspace& ws, hipStream_t stream) {
-  const bool big = s.nb > 1536;
-  if (s.D == 128) return big ? launch_select_t<128, 8>(s, ws, stream) : launch_select_t<128, 16>(s, ws, stream);
-  return big ? launch_select_t<64, 8>(s, ws, stream) : launch_select_t<64, 16>(s, ws, stream);
+  if (s.D == 128) return launch_select_t<128>(s, ws, stream);
+  return launch_select_t<64>(s, ws, stream);
 }
 
 
