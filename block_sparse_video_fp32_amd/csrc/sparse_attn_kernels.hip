@@ -521,15 +521,21 @@ __device__ __forceinline__ f32x16 tile_qk(const uint8_t* stage, int lane, const 
 // key(8 (i/4) + 4 hh + i % 4).
 __device__ __forceinline__ void tile_key_bias(float (&kb)[16], bool cen, int c, int half, int N, int nb,
                                               uint32_t sbits, int hh, float bias_full, float bias_tail) {
-  const int nvalid = cen ? 0 : min(kBlock, N - c * kBlock);
+  // One bit per key of the half tile: set = no term (selected centroid,
+  // block past n_b, or key past N).
+  const int nv = cen ? nb - 32 * c : min(kBlock, N - c * kBlock) - 32 * half;  // valid keys
+  uint32_t m = (nv >= 32) ? 0u : ~((1u << max(nv, 0)) - 1u);
+  if (cen) m |= sbits;
+  const float bval = cen ? bias_full : 0.0f;
+  const uint32_t sb = m >> (4 * hh);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int kap = 16 * ((i >> 2) & 1) + 8 * (i >> 3) + 4 * hh + (i & 3);
-    const bool ok_e = 32 * half + kap < nvalid;
-    const int cc = 32 * c + kap;
-    const bool ok_c = cc < nb && !((sbits >> kap) & 1u);
-    const float bc = (cc == nb - 1) ? bias_tail : bias_full;
-    kb[i] = cen ? (ok_c ? bc : -INFINITY) : (ok_e ? 0.0f : -INFINITY);
+  for (int i = 0; i < 16; ++i) kb[i] = ((sb >> (16 * ((i >> 2) & 1) + 8 * (i >> 3) + (i & 3))) & 1u) ? -INFINITY : bval;
+  // the centroid of a ragged last block carries log2 of its own row count
+  const int rt = nb - 1 - 32 * c;
+  if (cen && rt >= 0 && rt < 32 && !((m >> rt) & 1u) && bias_tail != bias_full) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (16 * ((i >> 2) & 1) + 8 * (i >> 3) + 4 * hh + (i & 3) == rt) kb[i] = bias_tail;
   }
 }
 
