@@ -433,8 +433,9 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
 //   S^T = K Q^T     D/16 v_mfma_f32_32x32x16_bf16
 //   P = exp2(S^T c1 + bias - mref), row sums in-lane (VALU)
 //   O^T += V^T P^T  D/16 MFMAs
-// Two waves run per SIMD, so one wave's exponentials overlap the other's
-// MFMAs.
+// Three waves run per SIMD (at most 168 VGPRs each, a two-stage ring so that
+// three workgroups fit a CU's LDS), so that the waves of one workgroup that
+// skip a half tile or wait at its barrier leave the SIMD to the others.
 //
 // LDS order of a half tile: 1 KB blocks of 64 lanes x 16 bytes, each the
 // A operand of one MFMA for lane = position:
@@ -587,7 +588,7 @@ __device__ __forceinline__ void tile_pv(const uint8_t* stage, int lane, const f3
 }
 
 template <int D, int S>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attend_kernel(
     Shape s, const uint16_t* __restrict__ q, uint16_t* __restrict__ out, Workspace ws) {
   constexpr int NK = D / 16;          // QK k-steps = K blocks = PV MFMAs per tile
   constexpr int NDT = D / 32;         // 32-row d tiles of O^T
@@ -906,9 +907,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// Ring depth: half tile u + 2 is requested while u is computed.  Measured
-// at N = 16384 and 32768, 2, 3 and 4 stages run within 1% of each other.
-constexpr int kAttendStages = 3;
+// Ring depth: half tile u + 1 is requested while u is computed.  At
+// N = 16384 and 32768, 2, 3 and 4 stages ran within 1% of each other at the
+// same occupancy; two stages (32 KB at D = 128) let three workgroups share a
+// CU, which is 6-9% faster than two.
+constexpr int kAttendStages = 2;
 
 template <int D, int S>
 hipError_t launch_attend_t(const Shape& s, const uint16_t* q, uint16_t* out, const Workspace& ws,
