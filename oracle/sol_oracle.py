@@ -22,7 +22,9 @@ What is computed, step by step, and where the pages state it:
    The packed conditioning prefix is kept as an exact KV sink (thakicloud
    post, same section; Star7 README, Sol: audio-range KV sink) and prefix
    query rows get full attention (Star7 README, Sol; aikraft.ru news,
-   section "Нововведения версии 2.0": exact_kv_and_rows).
+   section "Нововведения версии 2.0": exact_kv_and_rows).  The same news
+   item names a lighter mode, exact_kv, that keeps only the sink; with
+   prefix_rows=False the prefix query rows are routed like every other row.
 4. Combine.  Selected blocks are attended exactly; every unselected block is
    not dropped but contributes once through its K/V centroid, and both kinds
    of term share one softmax (Star7 README, Sol).  Each centroid logit gets a
@@ -44,7 +46,9 @@ notes of this repository):
   ratio; the 1e-6 keeps ratios such as 0.1 * 640 from rounding up), ties
   going to the lower block index;
 * the prefix sink (every key block holding a row < prefix_len) is OR-ed in
-  after ranking; every query block holding a prefix row is computed densely;
+  after ranking; every query block holding a prefix row is computed densely
+  (exact_kv_and_rows, the default), or, in exact_kv mode, routed by the same
+  rule as the other rows;
 * the centroid logit uses the individual query row: q_i . Kbar_c * scale;
 * the log-mass bias is log(n_c), n_c = valid rows of block c (64, or the
   tail count), i.e. the centroid counts as n_c copies of itself;
@@ -132,14 +136,19 @@ def route(
     tau: Optional[float] = 1.0,
     topk_ratio: Optional[float] = None,
     prefix_len: int = 0,
+    prefix_rows: bool = True,
 ) -> Dict[str, np.ndarray]:
     """Block selection from the score matrix S [B, H, n_b, n_b].
+
+    prefix_rows: query blocks holding prefix rows attend to every key block
+    (exact_kv_and_rows); False keeps only the key sink (exact_kv).
 
     Returns a dict with ``sel`` (bool [B, H, n_b, n_b]) and, per row, ``mu``,
     ``sigma``, ``thr`` (the tau threshold, or the k-th largest score in
     top-K mode) and ``cut``, the score value that separates kept from dropped
     blocks (thr in tau mode; in top-K mode the midpoint between the k-th and
-    (k+1)-th largest scores, -inf when k = n_b).  Both are NaN on dense rows.
+    (k+1)-th largest scores, -inf when k = n_b).  Both are NaN on dense
+    prefix rows.
     """
     B, H, nb, nb2 = S.shape
     assert nb == nb2
@@ -172,9 +181,9 @@ def route(
         cut = thr.copy()
     # Exact KV sink: every key block that holds a prefix row.
     sel[..., :pb] = True
-    # Prefix query rows see every key exactly.
-    sel[:, :, :pb, :] = True
-    if pb:
+    # Prefix query rows see every key exactly (exact_kv_and_rows).
+    if prefix_rows and pb:
+        sel[:, :, :pb, :] = True
         thr[:, :, :pb] = np.nan
         cut[:, :, :pb] = np.nan
     return dict(sel=sel, mu=mu, sigma=sigma, thr=thr, cut=cut)
@@ -237,13 +246,13 @@ def attend_block(
     return (W @ Vall) / W.sum(axis=1, keepdims=True)
 
 
-def _prepare(q, k, v, tau, topk_ratio, prefix_len, mask):
+def _prepare(q, k, v, tau, topk_ratio, prefix_len, mask, prefix_rows=True):
     B, N, H, D = q.shape
     qbar, kbar, vbar = pool(q), pool(k), pool(v)
     info = dict(qbar=qbar, kbar=kbar, vbar=vbar)
     if mask is None:
         S = block_scores(qbar, kbar)
-        r = route(S, tau=tau, topk_ratio=topk_ratio, prefix_len=prefix_len)
+        r = route(S, tau=tau, topk_ratio=topk_ratio, prefix_len=prefix_len, prefix_rows=prefix_rows)
         info.update(S=S, **r)
     else:
         info["sel"] = np.asarray(mask, dtype=bool)
@@ -259,6 +268,7 @@ def forward_blocks(
     tau: Optional[float] = 1.0,
     topk_ratio: Optional[float] = None,
     prefix_len: int = 0,
+    prefix_rows: bool = True,
     centroid: bool = True,
     logmass: bool = True,
     sm_scale: Optional[float] = None,
@@ -275,7 +285,7 @@ def forward_blocks(
     B, N, H, D = q.shape
     scale = (1.0 / math.sqrt(D)) if not sm_scale else float(sm_scale)
     if info is None:
-        info = _prepare(q, k, v, tau, topk_ratio, prefix_len, mask)
+        info = _prepare(q, k, v, tau, topk_ratio, prefix_len, mask, prefix_rows)
     sel = info["sel"]
     sizes = block_sizes(N)
     out = {}

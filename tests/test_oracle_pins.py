@@ -49,7 +49,7 @@ def dense_reference(q, k, v, scale=None):
     return out
 
 
-def brute_force(q, k, v, *, tau=1.0, topk_ratio=None, prefix_len=0, centroid=True, logmass=True):
+def brute_force(q, k, v, *, tau=1.0, topk_ratio=None, prefix_len=0, prefix_rows=True, centroid=True, logmass=True):
     """Independent small-N implementation: token-level scores, one masked
     softmax over [N exact keys | n_b centroids] per query row."""
     B, N, H, D = q.shape
@@ -82,7 +82,8 @@ def brute_force(q, k, v, *, tau=1.0, topk_ratio=None, prefix_len=0, centroid=Tru
                 else:
                     sel[a] = row >= row.mean() + tau * np.std(row)
             sel[:, :pb] = True
-            sel[:pb, :] = True
+            if prefix_rows:
+                sel[:pb, :] = True
             sels[b, h] = sel
             tok = sel[blk][:, blk]  # [N, N] token-level mask
             Kc = (ind.T @ K) / sizes[:, None]
@@ -181,6 +182,9 @@ def test_constant_key_blocks_need_the_log_mass_bias():
         (64, 1, 64, dict(tau=1.0)),
         (1, 1, 64, dict(tau=1.0)),
         (100, 3, 64, dict(tau=math.inf, prefix_len=10)),
+        (256, 2, 64, dict(tau=1.0, prefix_len=100, prefix_rows=False)),
+        (250, 2, 64, dict(topk_ratio=0.25, prefix_len=64, prefix_rows=False)),
+        (100, 3, 64, dict(tau=math.inf, prefix_len=10, prefix_rows=False)),
     ],
 )
 def test_brute_force_small(N, H, D, kw):
@@ -226,7 +230,8 @@ def test_route_hand_examples(case):
     if isinstance(tau, str):
         tau = float(tau)
     r = O.route(full[None, None], tau=tau if tau is not None else 1.0,
-                topk_ratio=case.get("topk_ratio"), prefix_len=case.get("prefix_len", 0))
+                topk_ratio=case.get("topk_ratio"), prefix_len=case.get("prefix_len", 0),
+                prefix_rows=case.get("prefix_rows", True))
     sel = r["sel"][0, 0]
     if "expect" in case:
         for a, want in enumerate(case["expect"]):
@@ -380,3 +385,22 @@ def test_generators_are_seeded_and_shaped():
     assert h[0].shape == (1, 1100, 2, 64)
     assert not np.array_equal(h[0][:, :64], h[1][:, :64])  # independent prefix
     np.testing.assert_array_equal(h[0][:, 64:], h[1][:, 64:])  # Q = K on video rows
+
+
+def test_exact_kv_mode_changes_only_prefix_rows():
+    """exact_kv (prefix_rows=False) differs from exact_kv_and_rows only on
+    query blocks that hold prefix rows; there the list is the rows' own
+    routing plus the sink, and with no prefix the two modes coincide."""
+    rng = np.random.default_rng(11)
+    S = rng.standard_normal((2, 3, 12, 12))
+    for kw in (dict(tau=1.0), dict(topk_ratio=0.25)):
+        a = O.route(S, prefix_len=130, **kw)["sel"]
+        b = O.route(S, prefix_len=130, prefix_rows=False, **kw)["sel"]
+        plain = O.route(S, **kw)["sel"]
+        pb = 3
+        np.testing.assert_array_equal(a[:, :, pb:], b[:, :, pb:])
+        assert a[:, :, :pb].all()
+        want = plain[:, :, :pb].copy()
+        want[..., :pb] = True
+        np.testing.assert_array_equal(b[:, :, :pb], want)
+        np.testing.assert_array_equal(O.route(S, prefix_rows=False, **kw)["sel"], plain)
