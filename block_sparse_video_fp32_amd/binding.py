@@ -28,12 +28,14 @@ __all__ = [
     "SA_ROUTE_TOPK",
     "SA_FLAG_CENTROID",
     "SA_FLAG_LOGMASS",
+    "SA_FLAG_EXACT_KV_ONLY",
 ]
 
 SA_ROUTE_TAU = 0
 SA_ROUTE_TOPK = 1
 SA_FLAG_CENTROID = 1
 SA_FLAG_LOGMASS = 2
+SA_FLAG_EXACT_KV_ONLY = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libsparse_attn.so"
@@ -159,7 +161,9 @@ class SparseAttnPlan:
     """A validated shape + routing configuration (host object).
 
     ``tau=-inf`` selects the dense path.  Exactly one of ``tau`` and
-    ``topk_ratio`` is used: ``topk_ratio`` wins when given.
+    ``topk_ratio`` is used: ``topk_ratio`` wins when given.  ``prefix_len``
+    rows form the exact KV sink; their query blocks attend densely unless
+    ``exact_kv_only`` (SA_FLAG_EXACT_KV_ONLY) routes them like the others.
     """
 
     def __init__(
@@ -172,6 +176,7 @@ class SparseAttnPlan:
         tau: Optional[float] = 1.0,
         topk_ratio: Optional[float] = None,
         prefix_len: int = 0,
+        exact_kv_only: bool = False,
         centroid: bool = True,
         logmass: bool = True,
         sm_scale: Optional[float] = None,
@@ -194,7 +199,8 @@ class SparseAttnPlan:
             p.tau = float(1.0 if tau is None else tau)
         p.prefix_len = int(prefix_len)
         p.sm_scale = float(sm_scale) if sm_scale else 0.0
-        p.flags = (SA_FLAG_CENTROID if centroid else 0) | (SA_FLAG_LOGMASS if logmass else 0)
+        p.flags = ((SA_FLAG_CENTROID if centroid else 0) | (SA_FLAG_LOGMASS if logmass else 0)
+                   | (SA_FLAG_EXACT_KV_ONLY if exact_kv_only else 0))
         handle = ctypes.c_void_p()
         _check(lib.sparse_attn_plan_create(ctypes.byref(p), ctypes.byref(handle)), "sparse_attn_plan_create")
         self._lib = lib
@@ -332,6 +338,7 @@ def sparse_attn(
     tau: Optional[float] = None,
     topk_ratio: Optional[float] = None,
     prefix_len: int = 0,
+    exact_kv_only: bool = False,
     centroid: bool = True,
     logmass: bool = True,
     sm_scale: Optional[float] = None,
@@ -354,6 +361,7 @@ def sparse_attn(
         tau=1.0 if (tau is None and topk_ratio is None) else tau,
         topk_ratio=topk_ratio,
         prefix_len=prefix_len,
+        exact_kv_only=exact_kv_only,
         centroid=centroid,
         logmass=logmass,
         sm_scale=sm_scale,

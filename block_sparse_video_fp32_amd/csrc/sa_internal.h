@@ -26,6 +26,7 @@ struct Shape {
   float bias_full;          // log2(64) when the log-mass bias is on, else 0
   float bias_tail;          // log2(tail) when on, else 0
   int centroid;             // centroid terms on
+  int prefix_rows;          // query blocks holding prefix rows are dense
 };
 
 // Device workspace sections (see the layout notes in sparse_attn.h).

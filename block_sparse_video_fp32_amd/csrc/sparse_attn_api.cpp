@@ -110,7 +110,7 @@ int validate_params(const sparse_attn_params& p) {
   if (p.prefix_len < 0 || p.prefix_len > p.N)
     return fail(SA_EINVAL, "prefix_len must be in [0, N] (got %d, N=%d)", p.prefix_len, p.N);
   if (!std::isfinite(p.sm_scale)) return fail(SA_EINVAL, "sm_scale must be finite");
-  if (p.flags & ~(SA_FLAG_CENTROID | SA_FLAG_LOGMASS))
+  if (p.flags & ~(SA_FLAG_CENTROID | SA_FLAG_LOGMASS | SA_FLAG_EXACT_KV_ONLY))
     return fail(SA_EINVAL, "unknown flag bits 0x%x", p.flags);
   return SA_OK;
 }
@@ -153,6 +153,7 @@ void build_plan(sparse_attn_plan* pl) {
   s.bias_full = logmass ? 6.0f : 0.0f;  // log2(64)
   s.bias_tail = logmass ? (float)std::log2((double)s.tail) : 0.0f;
   s.centroid = (p.flags & SA_FLAG_CENTROID) ? 1 : 0;
+  s.prefix_rows = (p.flags & SA_FLAG_EXACT_KV_ONLY) ? 0 : 1;
 
   sparse_attn_ws_layout& L = pl->layout;
   std::memset(&L, 0, sizeof(L));

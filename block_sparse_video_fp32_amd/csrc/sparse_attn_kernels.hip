@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
     if (a >= nb) break;
     const float* Srow = S + r * nb;
     int* list = ws.lists + (bh * nb + a) * (long long)nb;
-    if (s.dense || a < s.pb) {  // dense row: every block
+    if (s.dense || (a < s.pb && s.prefix_rows)) {  // dense row: every block
       for (int c = lane; c < nb; c += 64) list[c] = c;
       if (lane == 0) ws.counts[bh * nb + a] = nb;
       continue;

@@ -13,7 +13,8 @@
  *      a top-K ratio (comfyui-wiki "Spark-H3" news, 워크플로 section); key
  *      blocks holding rows of the packed prefix are always selected (exact KV
  *      sink) and query blocks holding prefix rows attend densely (Star7
- *      README, Sol; aikraft.ru Sol-Attn news, exact_kv_and_rows);
+ *      README, Sol; aikraft.ru Sol-Attn news, exact_kv_and_rows), or, with
+ *      SA_FLAG_EXACT_KV_ONLY, are routed like the others (exact_kv);
  *   4. selected blocks are attended exactly (bf16 QK^T and PV on MFMA);
  *      every unselected block contributes once through its centroid,
  *      logit q_i . Kbar_c * scale + log(n_c), value Vbar_c, where n_c is the
@@ -51,7 +52,7 @@ extern "C" {
 
 #define SA_BLOCK 64          /* rows per query / key block */
 #define SA_MAX_BLOCKS 2048   /* largest supported n_b = ceil(N / 64) */
-#define SA_ABI_VERSION 2
+#define SA_ABI_VERSION 3
 
 /* Routing modes (sparse_attn_params.route). */
 #define SA_ROUTE_TAU 0   /* S >= mean + tau * std; tau = -inf is the dense path */
@@ -60,6 +61,12 @@ extern "C" {
 /* Flags (sparse_attn_params.flags). */
 #define SA_FLAG_CENTROID 1u /* unselected blocks contribute through centroids */
 #define SA_FLAG_LOGMASS 2u  /* add log(n_c) to every centroid logit */
+/* Prefix mode exact_kv (aikraft.ru Sol-Attn news, section
+ * "Нововведения версии 2.0"): the prefix key blocks stay an exact sink for
+ * every query block, but query blocks holding prefix rows are routed like
+ * the others.  Without it (exact_kv_and_rows, the default) those query
+ * blocks attend to every key block. */
+#define SA_FLAG_EXACT_KV_ONLY 4u
 #define SA_FLAGS_DEFAULT (SA_FLAG_CENTROID | SA_FLAG_LOGMASS)
 
 /* Error codes. */

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.sparse_attn_abi_version() == 2
+    assert lib.sparse_attn_abi_version() == 3
 
 
 def _params(**kw):
@@ -84,7 +84,7 @@ def _create(lib, p):
         (dict(prefix_len=1025), SA_EINVAL),
         (dict(prefix_len=1024), 0),
         (dict(sm_scale=float("inf")), SA_EINVAL),
-        (dict(flags=4), SA_EINVAL),
+        (dict(flags=8), SA_EINVAL),
         (dict(in_stride_b=3 * 1024 * 128, in_stride_t=3 * 128, in_stride_h=64), 0),
         (dict(in_stride_b=1024 * 128, in_stride_t=130, in_stride_h=64), SA_EALIGN),
         (dict(in_stride_b=0, in_stride_t=128, in_stride_h=64), SA_EINVAL),
@@ -174,3 +174,11 @@ def test_plan_error_raises():
     with pytest.raises(binding.SparseAttnError) as e:
         binding.SparseAttnPlan(1, 128, 1, 96)
     assert e.value.code == SA_EUNSUPPORTED_SHAPE and "64 or 128" in str(e.value)
+
+
+def test_exact_kv_flag_is_accepted(lib):
+    from block_sparse_video_fp32_amd.binding import SA_FLAG_EXACT_KV_ONLY
+    assert SA_FLAG_EXACT_KV_ONLY == 4
+    assert _create(lib, _params(flags=3 | SA_FLAG_EXACT_KV_ONLY, prefix_len=100)) == 0
+    plan = binding.SparseAttnPlan(1, 1024, 2, 64, prefix_len=100, exact_kv_only=True)
+    assert plan.params.flags == 3 | SA_FLAG_EXACT_KV_ONLY

@@ -115,7 +115,10 @@ def check_output(got, ref, label=""):
 
 
 def oracle_kw(kw):
-    return {k: kw[k] for k in ("tau", "topk_ratio", "prefix_len", "centroid", "logmass", "sm_scale") if k in kw}
+    o = {k: kw[k] for k in ("tau", "topk_ratio", "prefix_len", "centroid", "logmass", "sm_scale") if k in kw}
+    if kw.get("exact_kv_only"):
+        o["prefix_rows"] = False  # exact_kv: the sink without dense prefix rows
+    return o
 
 
 def full_parity(q, k, v, **kw):
@@ -208,6 +211,8 @@ SMALL = [
     ("topk", dict(B=1, N=1500, H=2, D=128), dict(topk_ratio=0.25)),
     ("topk_prefix", dict(B=2, N=1100, H=2, D=64), dict(topk_ratio=0.1, prefix_len=100)),
     ("prefix_tau", dict(B=1, N=1024, H=3, D=128), dict(tau=1.0, prefix_len=64)),
+    ("exact_kv_tau", dict(B=1, N=1024, H=2, D=128), dict(tau=1.0, prefix_len=130, exact_kv_only=True)),
+    ("exact_kv_topk", dict(B=2, N=1100, H=2, D=64), dict(topk_ratio=0.1, prefix_len=100, exact_kv_only=True)),
     ("no_centroid", dict(B=1, N=1024, H=2, D=128), dict(tau=1.0, centroid=False)),
     ("no_logmass", dict(B=1, N=1024, H=2, D=64), dict(tau=1.0, logmass=False)),
     ("scale", dict(B=1, N=512, H=2, D=64), dict(tau=0.5, sm_scale=0.3)),
