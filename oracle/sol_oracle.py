@@ -31,6 +31,16 @@ What is computed, step by step, and where the pages state it:
    log-mass bias so that the centroid stands for the block's mass (Spark-H3
    news, Spark-Reweight bullet and its figure caption: mean pooling gives
    exp(E[x]) where the block's mass is E[exp(x)]).
+5. Reweight (optional, reweight=True).  Spark-Reweight (Spark-H3 news, same
+   bullet) replaces the mean-pooled K/V summaries by weighted summaries plus
+   a log-mass bias, scored against one anchor per head, the mean of the
+   video queries.  Reading: anchor a = mean of the query rows >= prefix_len
+   (all rows when there are none); per key block, x_j = a . k_j * scale and
+   w = softmax(x) over the block's rows; Ktilde = sum w_j k_j,
+   Vtilde = sum w_j v_j, bias = logsumexp(x) - a . Ktilde * scale.  For the
+   anchor itself the centroid term then equals the block's exact terms in
+   mass and value; for a block of equal keys it is the mean-pooled centroid
+   with bias log(n_c).
 
 Readings where the pages leave a step open (each is argued in the design
 notes of this repository):
@@ -82,6 +92,7 @@ __all__ = [
     "selection_lists",
     "attend_block",
     "forward",
+    "reweight_summaries",
     "forward_blocks",
 ]
 
@@ -214,12 +225,15 @@ def attend_block(
     scale: float,
     centroid: bool,
     logmass: bool,
+    cbias_head: Optional[np.ndarray] = None,
 ) -> np.ndarray:
     """Output rows of one query block of one head.
 
-    q_rows [n_a, D]; k_head, v_head [N, D]; kbar_head, vbar_head [n_b, D];
-    sel_row bool [n_b].  Exact logits for every valid key of a selected block,
-    one centroid logit per unselected block, one softmax over all of them.
+    q_rows [n_a, D]; k_head, v_head [N, D]; kbar_head, vbar_head [n_b, D]
+    (the centroid summaries); sel_row bool [n_b].  Exact logits for every
+    valid key of a selected block, one centroid logit per unselected block,
+    one softmax over all of them.  cbias_head [n_b], when given, is the
+    centroid bias (reweight mode) in place of log(n_c).
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     chosen = np.nonzero(sel_row)[0]
@@ -233,7 +247,9 @@ def attend_block(
     if centroid:
         missed = np.nonzero(~sel_row)[0]
         y = q_rows @ kbar_head[missed].T * scale
-        if logmass:
+        if cbias_head is not None:
+            y = y + cbias_head[missed][None, :]
+        elif logmass:
             y = y + np.log(sizes[missed].astype(np.float64))[None, :]
         logits.append(y)
         values.append(vbar_head[missed])
@@ -244,6 +260,40 @@ def attend_block(
     M = L.max(axis=1, keepdims=True)
     W = np.exp(L - M)
     return (W @ Vall) / W.sum(axis=1, keepdims=True)
+
+
+def reweight_summaries(q, k, v, prefix_len: int = 0, sm_scale: Optional[float] = None):
+    """Spark-Reweight summaries (reading in the module docstring).
+
+    Returns (anchor [B, H, D], ktilde [B, H, n_b, D], vtilde [B, H, n_b, D],
+    cbias [B, H, n_b]), all float64.  cbias is in natural-log units.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, N, H, D = q.shape
+    scale = (1.0 / math.sqrt(D)) if not sm_scale else float(sm_scale)
+    first = int(prefix_len) if 0 <= int(prefix_len) < N else 0
+    anchor = q[:, first:].mean(axis=1)  # [B, H, D]
+    nb = num_blocks(N)
+    sizes = block_sizes(N)
+    kt = np.empty((B, H, nb, D))
+    vt = np.empty((B, H, nb, D))
+    cb = np.empty((B, H, nb))
+    for b in range(B):
+        for h in range(H):
+            a = anchor[b, h]
+            for c in range(nb):
+                rows = slice(c * BLOCK, c * BLOCK + sizes[c])
+                kc, vc = k[b, rows, h], v[b, rows, h]
+                x = kc @ a * scale
+                m = x.max()
+                e = np.exp(x - m)
+                w = e / e.sum()
+                kt[b, h, c] = w @ kc
+                vt[b, h, c] = w @ vc
+                cb[b, h, c] = (m + math.log(e.sum())) - float(kt[b, h, c] @ a) * scale
+    return anchor, kt, vt, cb
 
 
 def _prepare(q, k, v, tau, topk_ratio, prefix_len, mask, prefix_rows=True):
@@ -271,6 +321,7 @@ def forward_blocks(
     prefix_rows: bool = True,
     centroid: bool = True,
     logmass: bool = True,
+    reweight: bool = False,
     sm_scale: Optional[float] = None,
     mask: Optional[np.ndarray] = None,
     info: Optional[dict] = None,
@@ -286,6 +337,11 @@ def forward_blocks(
     scale = (1.0 / math.sqrt(D)) if not sm_scale else float(sm_scale)
     if info is None:
         info = _prepare(q, k, v, tau, topk_ratio, prefix_len, mask, prefix_rows)
+    if reweight and "cbias" not in info:
+        info["anchor"], info["ktilde"], info["vtilde"], info["cbias"] = reweight_summaries(
+            q, k, v, prefix_len=prefix_len, sm_scale=sm_scale)
+    ksum = info["ktilde"] if reweight else info["kbar"]
+    vsum = info["vtilde"] if reweight else info["vbar"]
     sel = info["sel"]
     sizes = block_sizes(N)
     out = {}
@@ -295,13 +351,14 @@ def forward_blocks(
             q[b, rows, h, :],
             k[b, :, h, :],
             v[b, :, h, :],
-            info["kbar"][b, h],
-            info["vbar"][b, h],
+            ksum[b, h],
+            vsum[b, h],
             sel[b, h, a],
             sizes,
             scale=scale,
             centroid=centroid,
             logmass=logmass,
+            cbias_head=info["cbias"][b, h] if reweight else None,
         )
     return out, info
 

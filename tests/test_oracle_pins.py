@@ -404,3 +404,66 @@ def test_exact_kv_mode_changes_only_prefix_rows():
         want[..., :pb] = True
         np.testing.assert_array_equal(b[:, :, :pb], want)
         np.testing.assert_array_equal(O.route(S, prefix_rows=False, **kw)["sel"], plain)
+
+
+# ------------------------------------------------------------- Spark-Reweight
+
+
+def test_reweight_equal_keys_reduce_to_log_mass():
+    """A block whose keys are all equal has uniform anchor weights: the
+    weighted summaries are the means and the bias is log(n_c), so reweight
+    mode gives exactly the default (mean pooling + log-mass) output."""
+    rng = np.random.default_rng(21)
+    B, N, H, D = 1, 200, 2, 64
+    q = rng.standard_normal((B, N, H, D))
+    kb = rng.standard_normal((B, (N + 63) // 64, H, D))
+    k = np.repeat(kb, 64, axis=1)[:, :N]
+    v = rng.standard_normal((B, N, H, D))
+    for kw in (dict(tau=1.0), dict(topk_ratio=0.5, prefix_len=30)):
+        a, _ = O.forward(q, k, v, **kw)
+        b, info = O.forward(q, k, v, reweight=True, **kw)
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+        want = np.broadcast_to(np.log(O.block_sizes(N)), info["cbias"].shape)
+        np.testing.assert_allclose(info["cbias"], want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("prefix_len", [0, 70])
+def test_reweight_is_exact_for_the_anchor_query(prefix_len):
+    """For the anchor query itself (the mean of the rows >= prefix_len), the
+    reweighted centroid of a block carries that block's exact mass and
+    exact attention-weighted value, so dropping blocks to their centroids
+    leaves the anchor row's output unchanged.  The prefix rows are placed far
+    from the anchor so that an anchor taken over all rows would fail."""
+    rng = np.random.default_rng(22)
+    B, N, H, D = 1, 300, 1, 64
+    t_star = 150
+    a = rng.standard_normal(D) * 0.8
+    delta = rng.standard_normal((N, D))
+    delta[:prefix_len] += 6.0  # prefix rows: not part of the anchor
+    video = [t for t in range(prefix_len, N) if t != t_star]
+    delta[video] -= delta[video].mean(axis=0)
+    delta[t_star] = 0.0
+    q = (a[None, :] + delta)[None, :, None, :]
+    k = rng.standard_normal((B, N, H, D))
+    v = rng.standard_normal((B, N, H, D))
+    nb = (N + 63) // 64
+    full = np.ones((B, H, nb, nb), dtype=bool)
+    part = full.copy()
+    part[..., 1::2] = False  # half of the key blocks only through centroids
+    ref, _ = O.forward(q, k, v, mask=full, reweight=True, prefix_len=prefix_len)
+    got, info = O.forward(q, k, v, mask=part, reweight=True, prefix_len=prefix_len)
+    np.testing.assert_allclose(info["anchor"][0, 0], a, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[0, t_star, 0], ref[0, t_star, 0], rtol=0, atol=1e-10)
+    # other rows do change: the centroid is exact for the anchor only
+    assert np.abs(got[0, 0, 0] - ref[0, 0, 0]).max() > 1e-6
+
+
+def test_reweight_bias_is_the_weight_entropy():
+    """bias = logsumexp(x) - sum_j w_j x_j with w = softmax(x) is the entropy
+    of w: between 0 and log(n_c)."""
+    q, k, v = _rand(1, 300, 2, 64, seed=23)
+    _, kt, vt, cb = O.reweight_summaries(q * 2.0, k, v, prefix_len=10)
+    n = O.block_sizes(300)
+    assert (cb >= -1e-12).all()
+    assert (cb <= np.log(n)[None, None, :] + 1e-12).all()
+    assert np.isfinite(kt).all() and np.isfinite(vt).all()
