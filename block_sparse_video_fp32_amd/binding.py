@@ -29,6 +29,7 @@ __all__ = [
     "SA_FLAG_CENTROID",
     "SA_FLAG_LOGMASS",
     "SA_FLAG_EXACT_KV_ONLY",
+    "SA_FLAG_REWEIGHT",
 ]
 
 SA_ROUTE_TAU = 0
@@ -36,6 +37,7 @@ SA_ROUTE_TOPK = 1
 SA_FLAG_CENTROID = 1
 SA_FLAG_LOGMASS = 2
 SA_FLAG_EXACT_KV_ONLY = 4
+SA_FLAG_REWEIGHT = 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libsparse_attn.so"
@@ -80,6 +82,8 @@ class _Layout(ctypes.Structure):
         ("vbar_packed", ctypes.c_uint64),
         ("counts", ctypes.c_uint64),
         ("lists", ctypes.c_uint64),
+        ("anchor", ctypes.c_uint64),
+        ("cbias", ctypes.c_uint64),
         ("n_blocks", ctypes.c_int32),
         ("n_blocks_padded", ctypes.c_int32),
         ("tail_rows", ctypes.c_int32),
@@ -179,6 +183,7 @@ class SparseAttnPlan:
         exact_kv_only: bool = False,
         centroid: bool = True,
         logmass: bool = True,
+        reweight: bool = False,
         sm_scale: Optional[float] = None,
         in_strides: Optional[Tuple[int, int, int]] = None,
         out_strides: Optional[Tuple[int, int, int]] = None,
@@ -200,7 +205,7 @@ class SparseAttnPlan:
         p.prefix_len = int(prefix_len)
         p.sm_scale = float(sm_scale) if sm_scale else 0.0
         p.flags = ((SA_FLAG_CENTROID if centroid else 0) | (SA_FLAG_LOGMASS if logmass else 0)
-                   | (SA_FLAG_EXACT_KV_ONLY if exact_kv_only else 0))
+                   | (SA_FLAG_EXACT_KV_ONLY if exact_kv_only else 0) | (SA_FLAG_REWEIGHT if reweight else 0))
         handle = ctypes.c_void_p()
         _check(lib.sparse_attn_plan_create(ctypes.byref(p), ctypes.byref(handle)), "sparse_attn_plan_create")
         self._lib = lib
@@ -329,6 +334,15 @@ class SparseAttnPlan:
         vbp = self._view(ws, "vbar_packed", torch.bfloat16, (B, H, nbp // 32, 32 * D))
         return kp, vp, kbp, vbp
 
+    def reweight_views(self, ws):
+        """Reweight anchor fp32 [B, H, D] and centroid bias fp32 [B, H, n_bp]
+        (log2 units); written by the pool step with ``reweight=True``."""
+        import torch
+
+        B, N, H, D = self.shape
+        nbp = self.layout["n_blocks_padded"]
+        return self._view(ws, "anchor", torch.float32, (B, H, D)), self._view(ws, "cbias", torch.float32, (B, H, nbp))
+
 
 def sparse_attn(
     q,
@@ -341,6 +355,7 @@ def sparse_attn(
     exact_kv_only: bool = False,
     centroid: bool = True,
     logmass: bool = True,
+    reweight: bool = False,
     sm_scale: Optional[float] = None,
     out=None,
     return_route: bool = False,
@@ -363,6 +378,7 @@ def sparse_attn(
         prefix_len=prefix_len,
         exact_kv_only=exact_kv_only,
         centroid=centroid,
+        reweight=reweight,
         logmass=logmass,
         sm_scale=sm_scale,
         in_strides=(q.stride(0), q.stride(1), q.stride(2)),

@@ -27,6 +27,9 @@ struct Shape {
   float bias_tail;          // log2(tail) when on, else 0
   int centroid;             // centroid terms on
   int prefix_rows;          // query blocks holding prefix rows are dense
+  int reweight;             // Spark-Reweight centroids (never on the dense path)
+  float scale;              // softmax scale
+  int prefix_len;
 };
 
 // Device workspace sections (see the layout notes in sparse_attn.h).
@@ -40,9 +43,12 @@ struct Workspace {
   uint16_t* vbp;  // centroids Vbar^T in the same packed order, bf16
   int* counts;
   int* lists;
+  float* anchor;  // [B,H,D] reweight anchor
+  float* cbias;   // [B,H,nbp] reweight centroid bias, log2 units
 };
 
 hipError_t launch_pool_q(const Shape& s, const void* q, const Workspace& ws, hipStream_t stream);
+hipError_t launch_anchor(const Shape& s, const void* q, const Workspace& ws, hipStream_t stream);
 hipError_t launch_pack_kv(const Shape& s, const void* k, const void* v, const Workspace& ws,
                           hipStream_t stream);
 hipError_t launch_select(const Shape& s, const Workspace& ws, hipStream_t stream);

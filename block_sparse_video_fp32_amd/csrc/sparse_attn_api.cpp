@@ -110,7 +110,9 @@ int validate_params(const sparse_attn_params& p) {
   if (p.prefix_len < 0 || p.prefix_len > p.N)
     return fail(SA_EINVAL, "prefix_len must be in [0, N] (got %d, N=%d)", p.prefix_len, p.N);
   if (!std::isfinite(p.sm_scale)) return fail(SA_EINVAL, "sm_scale must be finite");
-  if (p.flags & ~(SA_FLAG_CENTROID | SA_FLAG_LOGMASS | SA_FLAG_EXACT_KV_ONLY))
+  if ((p.flags & SA_FLAG_REWEIGHT) && !(p.flags & SA_FLAG_CENTROID))
+    return fail(SA_EINVAL, "SA_FLAG_REWEIGHT needs SA_FLAG_CENTROID");
+  if (p.flags & ~(SA_FLAG_CENTROID | SA_FLAG_LOGMASS | SA_FLAG_EXACT_KV_ONLY | SA_FLAG_REWEIGHT))
     return fail(SA_EINVAL, "unknown flag bits 0x%x", p.flags);
   return SA_OK;
 }
@@ -154,6 +156,9 @@ void build_plan(sparse_attn_plan* pl) {
   s.bias_tail = logmass ? (float)std::log2((double)s.tail) : 0.0f;
   s.centroid = (p.flags & SA_FLAG_CENTROID) ? 1 : 0;
   s.prefix_rows = (p.flags & SA_FLAG_EXACT_KV_ONLY) ? 0 : 1;
+  s.reweight = ((p.flags & SA_FLAG_REWEIGHT) && !s.dense) ? 1 : 0;
+  s.scale = (float)scale;
+  s.prefix_len = p.prefix_len;
 
   sparse_attn_ws_layout& L = pl->layout;
   std::memset(&L, 0, sizeof(L));
@@ -171,6 +176,8 @@ void build_plan(sparse_attn_plan* pl) {
   L.vbar_packed = off; off = align256(off + cpacked);
   L.counts = off; off = align256(off + bh * s.nb * sizeof(int32_t));
   L.lists = off; off = align256(off + bh * s.nb * (uint64_t)s.nb * sizeof(int32_t));
+  L.anchor = off; off = align256(off + bh * p.D * sizeof(float));
+  L.cbias = off; off = align256(off + bh * s.nbp * sizeof(float));
   L.total_bytes = off;
   L.n_blocks = s.nb;
   L.n_blocks_padded = s.nbp;
@@ -193,6 +200,8 @@ sa::Workspace carve(const sparse_attn_plan* pl, void* ws) {
   w.vbp = reinterpret_cast<uint16_t*>(base + L.vbar_packed);
   w.counts = reinterpret_cast<int*>(base + L.counts);
   w.lists = reinterpret_cast<int*>(base + L.lists);
+  w.anchor = reinterpret_cast<float*>(base + L.anchor);
+  w.cbias = reinterpret_cast<float*>(base + L.cbias);
   return w;
 }
 
@@ -271,6 +280,9 @@ int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k,
   const sa::Workspace w = carve(plan, ws);
   hipStream_t st = (hipStream_t)stream;
   if ((rc = launched(sa::launch_pool_q(plan->shape, q, w, st), "pool_q"))) return rc;
+  if (plan->shape.reweight) {
+    if ((rc = launched(sa::launch_anchor(plan->shape, q, w, st), "anchor"))) return rc;
+  }
   if ((rc = launched(sa::launch_pack_kv(plan->shape, k, v, w, st), "pack_kv"))) return rc;
   return ok();
 }
@@ -308,6 +320,9 @@ int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void*
   hipStream_t st = (hipStream_t)stream;
   if (!plan->shape.dense) {
     if ((rc = launched(sa::launch_pool_q(plan->shape, q, w, st), "pool_q"))) return rc;
+  }
+  if (plan->shape.reweight) {
+    if ((rc = launched(sa::launch_anchor(plan->shape, q, w, st), "anchor"))) return rc;
   }
   if ((rc = launched(sa::launch_pack_kv(plan->shape, k, v, w, st), "pack_kv"))) return rc;
   if (!plan->shape.dense) {

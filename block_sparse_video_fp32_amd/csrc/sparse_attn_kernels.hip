@@ -142,6 +142,50 @@ __global__ __launch_bounds__(256) void pool_q_kernel(Shape s, const uint16_t* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// anchor: grid (H, B), 256 threads.  The reweight anchor of one head, the
+// mean of the query rows first .. N - 1, first = prefix_len (0 when no video
+// rows would remain): every block that starts at or after first adds
+// n_a * Qbar_a, and the rows of a block that straddles first are read from Q.
+// (Spark-H3 news, Spark-Reweight: one anchor per head from the video query
+// rows.)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void anchor_kernel(Shape s, const uint16_t* __restrict__ q, Workspace ws) {
+  constexpr int G = 256 / D;  // row groups
+  constexpr int U = 4;        // independent partial sums per thread
+  __shared__ float part[256];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const long long bh = (long long)b * s.H + h;
+  const int tid = threadIdx.x, d = tid % D, g = tid / D;
+  const int first = (s.prefix_len > 0 && s.prefix_len < s.N) ? s.prefix_len : 0;
+  const int af = (first + kBlock - 1) / kBlock;  // first block wholly at or after first
+  float acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = 0.0f;
+  const float* qb = ws.qbar + bh * s.nb * D + d;
+  int a = af + g;
+  for (; a + (U - 1) * G < s.nb; a += U * G) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = a + u * G;
+      acc[u] += (float)min(kBlock, s.N - c * kBlock) * qb[(long long)c * D];
+    }
+  }
+  for (; a < s.nb; a += G) acc[0] += (float)min(kBlock, s.N - a * kBlock) * qb[(long long)a * D];
+  const uint16_t* qp = q + (long long)b * s.isb + (long long)h * s.ish + d;
+  const int rend = min(af * kBlock, s.N);
+  for (int r = first + g; r < rend; r += G) acc[1] += bf16_bits_to_f32(qp[(long long)r * s.ist]);
+  part[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.0f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) t += part[k * D + tid];
+    ws.anchor[bh * D + tid] = t / (float)(s.N - first);
+  }
+}
+
 // Packed half-tile orders (see the file header): kappa(r) swaps bits 3 and 4
 // of a key index r (an involution).
 __device__ __forceinline__ int kappa(int r) { return (r & 7) | ((r & 8) << 1) | ((r & 16) >> 1); }
@@ -155,7 +199,10 @@ __device__ __forceinline__ int vt_key(int j, int l, int e) {
 // (zero past N) in LDS, writes the fp32 means Kbar, Vbar (sequential row
 // sums), the packed half tiles of K and V^T, and the bf16 centroids into
 // their packed centroid half tile (block j is centroid row j % 32 of centroid
-// half tile j / 32).  Blocks j >= n_b only zero their centroid rows.
+// half tile j / 32).  In reweight mode the packed centroids are the
+// anchor-weighted summaries and the block's bias goes to cbias; the fp32
+// means are still written (routing uses them).  Blocks j >= n_b only zero
+// their centroid rows (and bias).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* __restrict__ k,
@@ -165,6 +212,9 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
   constexpr int HT = 32 * D; // elements of one packed half tile
   __shared__ __attribute__((aligned(16))) uint16_t Kl[64 * LS];
   __shared__ __attribute__((aligned(16))) uint16_t Vl[64 * LS];
+  __shared__ float al[D];   // reweight anchor
+  __shared__ float wl[64];  // reweight row weights
+  __shared__ float red[8];
 
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const long long bh = (long long)b * s.H + h;
@@ -184,8 +234,10 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
       kc[kc_index(tid)] = 0;
       vc[vc_index(tid)] = 0;
     }
+    if (s.reweight && tid == 0) ws.cbias[bh * s.nbp + j] = 0.0f;
     return;
   }
+  if (s.reweight && tid < D) al[tid] = ws.anchor[bh * D + tid];
 
   const int n = min(kBlock, s.N - j * kBlock);
   const long long base = (long long)b * s.isb + (long long)h * s.ish + (long long)j * kBlock * s.ist;
@@ -203,18 +255,79 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
   }
   __syncthreads();
 
+  // Spark-Reweight (Spark-H3 news): row weights w = softmax(x) with
+  // x_r = scale * anchor . k_r over the block's rows, in log2 units.
+  // Four threads per row, each over every fourth pair of dimensions.
+  if (s.reweight) {
+    const int row = tid >> 2, p4 = tid & 3;
+    const uint32_t* kr = reinterpret_cast<const uint32_t*>(Kl + row * LS);
+    float xr = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+      const int pr = p4 + 4 * i;
+      const uint32_t two = kr[pr];
+      xr += al[2 * pr] * bf16_bits_to_f32(two & 0xffffu) + al[2 * pr + 1] * bf16_bits_to_f32(two >> 16);
+    }
+    xr += __shfl_xor(xr, 1);
+    xr += __shfl_xor(xr, 2);
+    if (p4 == 0) wl[row] = xr * s.c1;
+    __syncthreads();
+    if (tid < 64) {
+      const float xv = tid < n ? wl[tid] : -INFINITY;
+      float m = xv;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      const float e = tid < n ? exp2f(xv - m) : 0.0f;
+      float z = e;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+      wl[tid] = e / z;
+      if (tid == 0) {
+        red[0] = m;
+        red[1] = z;
+      }
+    }
+    __syncthreads();
+  }
+
+  // Block means (fp32, sequential over rows); with reweight the packed
+  // centroids hold the weighted sums Ktilde, Vtilde instead.
+  float kdot = 0.0f;  // anchor . Ktilde, this thread's dimension
   if (tid < 2 * D) {
     const uint16_t* src = (tid < D) ? Kl : Vl;
     const int d = tid % D;
-    float sum = 0.0f;
-    for (int row = 0; row < n; ++row) sum += bf16_bits_to_f32(src[row * LS + d]);
+    float sum = 0.0f, wsum = 0.0f;
+    if (s.reweight) {
+      for (int row = 0; row < n; ++row) {
+        const float x = bf16_bits_to_f32(src[row * LS + d]);
+        sum += x;
+        wsum += wl[row] * x;
+      }
+    } else {
+      for (int row = 0; row < n; ++row) sum += bf16_bits_to_f32(src[row * LS + d]);
+    }
     const float mean = sum / (float)n;
+    const float cval = s.reweight ? wsum : mean;
     if (tid < D) {
       ws.kbar[(bh * s.nb + j) * D + d] = mean;
-      kc[kc_index(d)] = (uint16_t)f32_to_bf16_bits(mean);
+      kc[kc_index(d)] = (uint16_t)f32_to_bf16_bits(cval);
+      kdot = al[d] * wsum;
     } else {
       ws.vbar[(bh * s.nb + j) * D + d] = mean;
-      vc[vc_index(d)] = (uint16_t)f32_to_bf16_bits(mean);
+      vc[vc_index(d)] = (uint16_t)f32_to_bf16_bits(cval);
+    }
+  }
+  // bias = logsumexp(x) - scale * anchor . Ktilde, in log2 units.
+  if (s.reweight) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) kdot += __shfl_xor(kdot, o);
+    if ((tid & 63) == 0 && tid < D) red[2 + (tid >> 6)] = kdot;
+    __syncthreads();
+    if (tid == 0) {
+      float ak = 0.0f;
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) ak += red[2 + k];
+      ws.cbias[bh * s.nbp + j] = red[0] + log2f(red[1]) - s.c1 * ak;
     }
   }
 
@@ -540,6 +653,24 @@ __device__ __forceinline__ void tile_key_bias(float (&kb)[16], bool cen, int c, 
   }
 }
 
+// The per-key terms of a centroid half tile in reweight mode: the bias of
+// each unselected block comes from the head's table cbt (log2 units) instead
+// of log2(n_c).  Four consecutive registers hold four consecutive keys.
+__device__ __forceinline__ void tile_key_bias_rw(float (&kb)[16], int c, int nb, uint32_t sbits, int hh,
+                                                 const float* cbt) {
+  const int nv = nb - 32 * c;
+  const uint32_t m = ((nv >= 32) ? 0u : ~((1u << max(nv, 0)) - 1u)) | sbits;
+  const uint32_t sb = m >> (4 * hh);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int k0 = 16 * (g & 1) + 8 * (g >> 1);
+    const float4 t = *reinterpret_cast<const float4*>(cbt + 32 * c + k0 + 4 * hh);
+    const float tv[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kb[4 * g + e] = ((sb >> (k0 + e)) & 1u) ? -INFINITY : tv[e];
+  }
+}
+
 // Maximum logit of this lane's query over one half tile.
 __device__ __forceinline__ float tile_row_max(const f32x16& sacc, const float (&kb)[16], float c1) {
   float m = -INFINITY;
@@ -587,7 +718,7 @@ __device__ __forceinline__ void tile_pv(const uint8_t* stage, int lane, const f3
   __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
 }
 
-template <int D, int S>
+template <int D, int S, bool RW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attend_kernel(
     Shape s, const uint16_t* __restrict__ q, uint16_t* __restrict__ out, Workspace ws) {
   constexpr int NK = D / 16;          // QK k-steps = K blocks = PV MFMAs per tile
@@ -602,6 +733,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   __shared__ uint16_t ulist[SA_MAX_BLOCKS];  // union of the two lists
   __shared__ uint16_t uct[NW];               // centroid half tiles either needs
   __shared__ int info[8];
+  __shared__ __attribute__((aligned(16))) float cbs[RW ? SA_MAX_BLOCKS : 4];  // reweight centroid biases
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -647,6 +779,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       info[4] = has1 ? 0 : 2 * nb;
     }
   } else {
+    if (RW)
+      for (int i = tid; i < s.nbp; i += 256) cbs[i] = ws.cbias[bh * s.nbp + i];
     const int cnt0 = min(max(ws.counts[bh * nb + a0], 0), nb);
     const int cnt1 = has1 ? min(max(ws.counts[bh * nb + a0 + 1], 0), nb) : 0;
     for (int i = tid; i < 2 * NW; i += 256) sel[i / NW][i % NW] = 0u;
@@ -808,7 +942,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   auto ring_next = [&]() { st = (st == S - 1) ? 0 : st + 1; };
   auto bias_of = [&](int u, int eu, float (&kb)[16]) {
     const bool cen = u >= TE;
-    tile_key_bias(kb, cen, eu & 0xfff, u & 1, N, nb, sel[x][cen ? (eu & (NW - 1)) : 0], hh, bias_full, bias_tail);
+    if (RW && cen)
+      tile_key_bias_rw(kb, eu & 0xfff, nb, sel[x][eu & (NW - 1)], hh, cbs);
+    else
+      tile_key_bias(kb, cen, eu & 0xfff, u & 1, N, nb, sel[x][cen ? (eu & (NW - 1)) : 0], hh, bias_full,
+                    bias_tail);
   };
 
   // Q and the lists are in registers / LDS before the first copy is issued.
@@ -913,15 +1051,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // CU, which is 6-9% faster than two.
 constexpr int kAttendStages = 2;
 
-template <int D, int S>
+template <int D, int S, bool RW>
 hipError_t launch_attend_t(const Shape& s, const uint16_t* q, uint16_t* out, const Workspace& ws,
                            hipStream_t stream) {
   constexpr int bytes = S * (D / 8) * 1024;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, S>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, S, RW>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((long long)s.B * s.H * ((s.nb + 1) / 2)));
-  hipLaunchKernelGGL((attend_kernel<D, S>), grid, dim3(256), bytes, stream, s, q, out, ws);
+  hipLaunchKernelGGL((attend_kernel<D, S, RW>), grid, dim3(256), bytes, stream, s, q, out, ws);
   return hipGetLastError();
 }
 
@@ -949,6 +1087,16 @@ hipError_t launch_pool_q(const Shape& s, const void* q, const Workspace& ws, hip
   return hipGetLastError();
 }
 
+hipError_t launch_anchor(const Shape& s, const void* q, const Workspace& ws, hipStream_t stream) {
+  dim3 grid(s.H, s.B);
+  const auto* qq = static_cast<const uint16_t*>(q);
+  if (s.D == 128)
+    hipLaunchKernelGGL(anchor_kernel<128>, grid, dim3(256), 0, stream, s, qq, ws);
+  else
+    hipLaunchKernelGGL(anchor_kernel<64>, grid, dim3(256), 0, stream, s, qq, ws);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_kv(const Shape& s, const void* k, const void* v, const Workspace& ws,
                           hipStream_t stream) {
   dim3 grid(s.nbp, s.H, s.B);
@@ -970,8 +1118,14 @@ hipError_t launch_select(const Shape& s, const Workspace& ws, hipStream_t stream
 hipError_t launch_attend(const Shape& s, const void* q, void* out, const Workspace& ws, hipStream_t stream) {
   const auto* qq = static_cast<const uint16_t*>(q);
   auto* oo = static_cast<uint16_t*>(out);
-  if (s.D == 128) return launch_attend_t<128, kAttendStages>(s, qq, oo, ws, stream);
-  return launch_attend_t<64, kAttendStages>(s, qq, oo, ws, stream);
+  // Reweight mode is its own instantiation, so that the default kernel
+  // carries none of its registers or LDS.
+  if (s.reweight) {
+    if (s.D == 128) return launch_attend_t<128, kAttendStages, true>(s, qq, oo, ws, stream);
+    return launch_attend_t<64, kAttendStages, true>(s, qq, oo, ws, stream);
+  }
+  if (s.D == 128) return launch_attend_t<128, kAttendStages, false>(s, qq, oo, ws, stream);
+  return launch_attend_t<64, kAttendStages, false>(s, qq, oo, ws, stream);
 }
 
 }  // namespace sa

@@ -67,6 +67,16 @@ extern "C" {
  * the others.  Without it (exact_kv_and_rows, the default) those query
  * blocks attend to every key block. */
 #define SA_FLAG_EXACT_KV_ONLY 4u
+/* Spark-Reweight (comfyui-wiki "Spark-H3" news, Spark-Reweight bullet and
+ * the compression-branch figure caption): every centroid is the
+ * anchor-weighted summary of its block instead of its mean, with a bias that
+ * restores the block's mass, scored against one anchor per head, the mean of
+ * the video query rows (rows >= prefix_len, all rows if there are none).
+ * With x_j = anchor . k_j * scale over the block's rows and
+ * w = softmax(x): Ktilde = sum w_j k_j, Vtilde = sum w_j v_j,
+ * bias = logsumexp(x) - anchor . Ktilde * scale, used in place of log(n_c).
+ * Requires SA_FLAG_CENTROID; routing still uses the block means. */
+#define SA_FLAG_REWEIGHT 8u
 #define SA_FLAGS_DEFAULT (SA_FLAG_CENTROID | SA_FLAG_LOGMASS)
 
 /* Error codes. */
@@ -109,10 +119,16 @@ typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
  *   v_packed          bf16, same tiling for V^T: in a half tile, element
  *                     ((m*64 + l)*8 + e) with m = 2 dt + j holds
  *                     V[16 (e/4) + 8 j + 4 (l/32) + e % 4][32 dt + l % 32].
- *   kbar_packed,      bf16 centroids (the means rounded to nearest even),
- *   vbar_packed       [B, H, n_bp/32] half tiles in the same two orders;
- *                     block c is row c % 32 of half tile c / 32; rows of
- *                     blocks >= n_b are zero (n_bp = n_b rounded up to 64).
+ *   kbar_packed,      bf16 centroids (the means rounded to nearest even;
+ *   vbar_packed       with SA_FLAG_REWEIGHT the weighted summaries Ktilde,
+ *                     Vtilde), [B, H, n_bp/32] half tiles in the same two
+ *                     orders; block c is row c % 32 of half tile c / 32;
+ *                     rows of blocks >= n_b are zero (n_bp = n_b rounded up
+ *                     to 64).
+ *   anchor            fp32 [B, H, D]: the reweight anchor (written only with
+ *                     SA_FLAG_REWEIGHT, off the dense path).
+ *   cbias             fp32 [B, H, n_bp]: the reweight centroid bias of each
+ *                     block in log2 units (bias / ln 2); same condition.
  * After sparse_attn_select:
  *   counts            int32 [B, H, n_b]: selected key blocks per query block.
  *   lists             int32 [B, H, n_b, n_b]: the selected key blocks in
@@ -124,6 +140,7 @@ typedef struct sparse_attn_ws_layout {
   uint64_t k_packed, v_packed;
   uint64_t kbar_packed, vbar_packed;
   uint64_t counts, lists;
+  uint64_t anchor, cbias;
   int32_t n_blocks;        /* n_b */
   int32_t n_blocks_padded; /* n_bp */
   int32_t tail_rows;       /* valid rows of block n_b - 1 */

@@ -84,7 +84,7 @@ def _create(lib, p):
         (dict(prefix_len=1025), SA_EINVAL),
         (dict(prefix_len=1024), 0),
         (dict(sm_scale=float("inf")), SA_EINVAL),
-        (dict(flags=8), SA_EINVAL),
+        (dict(flags=16), SA_EINVAL),
         (dict(in_stride_b=3 * 1024 * 128, in_stride_t=3 * 128, in_stride_h=64), 0),
         (dict(in_stride_b=1024 * 128, in_stride_t=130, in_stride_h=64), SA_EALIGN),
         (dict(in_stride_b=0, in_stride_t=128, in_stride_h=64), SA_EINVAL),
@@ -114,12 +114,13 @@ def test_workspace_layout_matches_documented_sizes():
     nb = 16
     assert L["n_blocks"] == nb and L["n_blocks_padded"] == 64
     assert L["tail_rows"] == 1000 - 64 * 15 and L["prefix_blocks"] == 2 and L["dense"] == 0
-    names = ("qbar", "kbar", "vbar", "k_packed", "v_packed", "kbar_packed", "vbar_packed", "counts", "lists")
+    names = ("qbar", "kbar", "vbar", "k_packed", "v_packed", "kbar_packed", "vbar_packed", "counts", "lists",
+             "anchor", "cbias")
     offs = sorted((L[n], n) for n in names)
     sizes = dict(qbar=2 * 3 * nb * 128 * 4, kbar=2 * 3 * nb * 128 * 4, vbar=2 * 3 * nb * 128 * 4,
                  k_packed=2 * 3 * nb * 64 * 128 * 2, v_packed=2 * 3 * nb * 64 * 128 * 2,
                  kbar_packed=2 * 3 * 64 * 128 * 2, vbar_packed=2 * 3 * 64 * 128 * 2,
-                 counts=2 * 3 * nb * 4, lists=2 * 3 * nb * nb * 4)
+                 counts=2 * 3 * nb * 4, lists=2 * 3 * nb * nb * 4, anchor=2 * 3 * 128 * 4, cbias=2 * 3 * 64 * 4)
     for (o, n), (o2, _) in zip(offs, offs[1:] + [(L["total_bytes"], "end")]):
         assert o % 256 == 0
         assert o2 - o >= sizes[n]
@@ -182,3 +183,11 @@ def test_exact_kv_flag_is_accepted(lib):
     assert _create(lib, _params(flags=3 | SA_FLAG_EXACT_KV_ONLY, prefix_len=100)) == 0
     plan = binding.SparseAttnPlan(1, 1024, 2, 64, prefix_len=100, exact_kv_only=True)
     assert plan.params.flags == 3 | SA_FLAG_EXACT_KV_ONLY
+
+
+def test_reweight_flag_needs_centroids(lib):
+    from block_sparse_video_fp32_amd.binding import SA_FLAG_REWEIGHT
+    assert SA_FLAG_REWEIGHT == 8
+    assert _create(lib, _params(flags=3 | SA_FLAG_REWEIGHT)) == 0
+    assert _create(lib, _params(flags=2 | SA_FLAG_REWEIGHT)) == SA_EINVAL  # centroids off
+    assert "SA_FLAG_CENTROID" in lib.sparse_attn_last_error().decode()

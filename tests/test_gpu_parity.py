@@ -115,7 +115,8 @@ def check_output(got, ref, label=""):
 
 
 def oracle_kw(kw):
-    o = {k: kw[k] for k in ("tau", "topk_ratio", "prefix_len", "centroid", "logmass", "sm_scale") if k in kw}
+    o = {k: kw[k] for k in ("tau", "topk_ratio", "prefix_len", "centroid", "logmass", "reweight", "sm_scale")
+         if k in kw}
     if kw.get("exact_kv_only"):
         o["prefix_rows"] = False  # exact_kv: the sink without dense prefix rows
     return o
@@ -199,6 +200,39 @@ def test_pooled_means_and_packed_tiles(N, D):
             assert (ck[nb:] == 0).all() and (cv[nb:] == 0).all()
 
 
+@pytest.mark.parametrize("N,D,prefix_len", [(1100, 64, 100), (1024, 128, 0), (300, 128, 300), (777, 128, 128)])
+def test_reweight_summaries(N, D, prefix_len):
+    """Anchor, centroid bias and the packed Ktilde / Vtilde centroids against
+    the oracle's fp64 summaries; the fp32 means stay the block means."""
+    q, k, v = inputs.clustered(2, N, 2, D, seed=N + D) if N >= 256 else inputs.iid(2, N, 2, D, seed=N)
+    run = GpuRun(q, k, v, tau=1.0, prefix_len=prefix_len, reweight=True)
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    anchor, kt, vt, cb = O.reweight_summaries(qf, kf, vf, prefix_len=prefix_len)
+    ga, gcb = (t.cpu().numpy().astype(np.float64) for t in run.plan.reweight_views(run.ws))
+    nb = O.num_blocks(N)
+    # fp32 block sums then a sum over blocks: (64 + n_b) roundings of |q|max
+    bound = 2 * (64 + nb) * 2.0**-24 * np.abs(qf).max()
+    assert np.abs(ga - anchor).max() <= bound, np.abs(ga - anchor).max()
+    # bias: log2 units on the GPU; fp32 dot products of length D
+    err = np.abs(gcb[:, :, :nb] * math.log(2.0) - cb)
+    print(f"  cbias max err {err.max():.3e}", flush=True)
+    assert err.max() <= 1e-3
+    assert (gcb[:, :, nb:] == 0).all()
+    kb = run.plan.pooled_views(run.ws)[1].float().cpu().numpy()
+    assert np.abs(kb - O.pool(kf)).max() <= 2 * 64 * 2.0**-24 * np.abs(kf).max()
+    _, _, kbp, vbp = (t.float().cpu().numpy() for t in run.plan.packed_views(run.ws))
+    for b in range(2):
+        for h in range(2):
+            ck = np.concatenate([_unpack_k(t, D) for t in kbp[b, h]])
+            cv = np.concatenate([_unpack_vt(t, D) for t in vbp[b, h]])
+            for got, ref in ((ck[:nb], kt[b, h]), (cv[:nb], vt[b, h])):
+                # one bf16 rounding of an fp32 sum: at most one unit in the
+                # last place (2^-7 relative) plus the fp32 summation error
+                tol = 2.0**-7 * np.abs(ref) + 1e-4 * np.abs(ref).max()
+                assert (np.abs(got - ref) <= tol).all(), np.abs(got - ref).max()
+            assert (ck[nb:] == 0).all() and (cv[nb:] == 0).all()
+
+
 # ---------------------------------------------------- small, every output row
 
 
@@ -213,6 +247,12 @@ SMALL = [
     ("prefix_tau", dict(B=1, N=1024, H=3, D=128), dict(tau=1.0, prefix_len=64)),
     ("exact_kv_tau", dict(B=1, N=1024, H=2, D=128), dict(tau=1.0, prefix_len=130, exact_kv_only=True)),
     ("exact_kv_topk", dict(B=2, N=1100, H=2, D=64), dict(topk_ratio=0.1, prefix_len=100, exact_kv_only=True)),
+    ("reweight_tau", dict(B=1, N=1024, H=2, D=128), dict(tau=1.0, reweight=True)),
+    ("reweight_prefix_tail", dict(B=2, N=1100, H=2, D=64), dict(tau=1.0, prefix_len=100, reweight=True)),
+    ("reweight_topk", dict(B=1, N=1500, H=2, D=128), dict(topk_ratio=0.25, prefix_len=128, reweight=True)),
+    ("reweight_exact_kv", dict(B=1, N=1000, H=3, D=64), dict(tau=0.5, prefix_len=70, exact_kv_only=True,
+                                                              reweight=True)),
+    ("reweight_dense", dict(B=1, N=777, H=2, D=128), dict(tau=-math.inf, reweight=True)),
     ("no_centroid", dict(B=1, N=1024, H=2, D=128), dict(tau=1.0, centroid=False)),
     ("no_logmass", dict(B=1, N=1024, H=2, D=64), dict(tau=1.0, logmass=False)),
     ("scale", dict(B=1, N=512, H=2, D=64), dict(tau=0.5, sm_scale=0.3)),
