@@ -41,6 +41,18 @@ What is computed, step by step, and where the pages state it:
    anchor itself the centroid term then equals the block's exact terms in
    mass and value; for a block of equal keys it is the mean-pooled centroid
    with bias log(n_c).
+6. INT8 QK^T (optional, int8_qk=True).  The thakicloud post (section
+   실제 실험 결과) describes an int8 QK path that quantises only each key
+   block's residual about the block mean and keeps the mean term exact in
+   bf16 (the Star7 README's 注意力模式 table lists QK-int8 modes with FP32
+   softmax).  Reading: base_c = the block's fp32 key mean (rows summed in
+   order) rounded to bf16; r = k - base_c; one scale per key block,
+   s_c = max |r| / 127 over its valid rows and all dimensions; residual
+   codes rint(r / s_c) clipped to [-127, 127]; one scale per query row,
+   s_q = max_d |q| / 127, codes rint(q / s_q).  An exact-block logit is
+   scale * (q . base_c + s_q * s_c * (q8 . r8)), q unquantised in the first
+   term.  Codes are decided in float32, the precision the kernel uses;
+   centroid logits are unchanged.
 
 Readings where the pages leave a step open (each is argued in the design
 notes of this repository):
@@ -93,6 +105,7 @@ __all__ = [
     "attend_block",
     "forward",
     "reweight_summaries",
+    "int8_qk_codes",
     "forward_blocks",
 ]
 
@@ -226,6 +239,7 @@ def attend_block(
     centroid: bool,
     logmass: bool,
     cbias_head: Optional[np.ndarray] = None,
+    int8_head: Optional[dict] = None,
 ) -> np.ndarray:
     """Output rows of one query block of one head.
 
@@ -233,7 +247,9 @@ def attend_block(
     (the centroid summaries); sel_row bool [n_b].  Exact logits for every
     valid key of a selected block, one centroid logit per unselected block,
     one softmax over all of them.  cbias_head [n_b], when given, is the
-    centroid bias (reweight mode) in place of log(n_c).
+    centroid bias (reweight mode) in place of log(n_c).  int8_head, when
+    given, holds this head's INT8 QK^T quantities (qcode, qscale for these
+    rows; kbase, kscale, kcode of the head) and sets the exact logits.
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     chosen = np.nonzero(sel_row)[0]
@@ -242,7 +258,10 @@ def attend_block(
     ) if len(chosen) else np.zeros(0, dtype=np.int64)
     kx = np.asarray(k_head[keys], dtype=np.float64)
     vx = np.asarray(v_head[keys], dtype=np.float64)
-    logits = [q_rows @ kx.T * scale]
+    if int8_head is None:
+        logits = [q_rows @ kx.T * scale]
+    else:
+        logits = [int8_logits(q_rows, keys, int8_head) * scale]
     values = [vx]
     if centroid:
         missed = np.nonzero(~sel_row)[0]
@@ -296,6 +315,70 @@ def reweight_summaries(q, k, v, prefix_len: int = 0, sm_scale: Optional[float] =
     return anchor, kt, vt, cb
 
 
+def int8_logits(q_rows, keys, h):
+    """Unscaled INT8 QK^T logits q . base_c + s_q s_c (q8 . r8) of the query
+    rows against the keys ``keys`` of one head (reading 6)."""
+    blk = np.asarray(keys, dtype=np.int64) // BLOCK
+    mean_term = np.asarray(q_rows, dtype=np.float64) @ np.asarray(h["kbase"], dtype=np.float64)[blk].T
+    dots = h["qcode"].astype(np.int64) @ h["kcode"][keys].astype(np.int64).T  # exact integers
+    sq = np.asarray(h["qscale"], dtype=np.float64)[:, None]
+    sk = np.asarray(h["kscale"], dtype=np.float64)[blk][None, :]
+    return mean_term + sq * sk * dots
+
+
+def _bf16_round(x):
+    """float32 -> nearest bfloat16 value (ties to even), as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return bits.astype(np.uint32).view(np.float32)
+
+
+def int8_qk_codes(q, k, residual: bool = True):
+    """INT8 QK^T quantities (reading 6 in the module docstring), in float32.
+
+    Returns a dict: kbase [B, H, n_b, D] (bf16 block means; zero when
+    residual=False, which quantises whole keys instead), kscale [B, H, n_b],
+    kcode [B, N, H, D] int8 residual codes, qscale [B, N, H] and
+    qcode [B, N, H, D] int8.
+    """
+    q = np.asarray(q, dtype=np.float32)
+    k = np.asarray(k, dtype=np.float32)
+    B, N, H, D = k.shape
+    nb = num_blocks(N)
+    sizes = block_sizes(N)
+    kp = np.zeros((B, nb * BLOCK, H, D), dtype=np.float32)
+    kp[:, :N] = k
+    kb = kp.reshape(B, nb, BLOCK, H, D)
+    valid = (np.arange(nb * BLOCK) < N).reshape(nb, BLOCK)
+    if residual:
+        acc = np.zeros((B, nb, H, D), dtype=np.float32)
+        for r in range(BLOCK):  # rows in order; padded rows add +0
+            acc = acc + kb[:, :, r]
+        mean = acc / sizes.astype(np.float32)[None, :, None, None]
+        base = _bf16_round(mean)
+    else:
+        base = np.zeros((B, nb, H, D), dtype=np.float32)
+    res = kb - base[:, :, None]
+    res = np.where(valid[None, :, :, None, None], res, np.float32(0))
+    amax = np.abs(res).max(axis=(2, 4))  # [B, nb, H]
+    ks = amax / np.float32(127)
+    safe = np.where(ks > 0, ks, np.float32(1))
+    code = np.rint(res / safe[:, :, None, :, None])
+    code = np.where(ks[:, :, None, :, None] > 0, np.clip(code, -127, 127), 0)
+    kcode = code.reshape(B, nb * BLOCK, H, D)[:, :N].astype(np.int8)
+    qs = np.abs(q).max(axis=3) / np.float32(127)  # [B, N, H]
+    qsafe = np.where(qs > 0, qs, np.float32(1))
+    qcode = np.where(qs[..., None] > 0, np.clip(np.rint(q / qsafe[..., None]), -127, 127), 0).astype(np.int8)
+    return dict(
+        kbase=base.transpose(0, 2, 1, 3).copy(),
+        kscale=ks.transpose(0, 2, 1).copy(),
+        kcode=kcode,
+        qscale=qs,
+        qcode=qcode,
+    )
+
+
 def _prepare(q, k, v, tau, topk_ratio, prefix_len, mask, prefix_rows=True):
     B, N, H, D = q.shape
     qbar, kbar, vbar = pool(q), pool(k), pool(v)
@@ -322,6 +405,7 @@ def forward_blocks(
     centroid: bool = True,
     logmass: bool = True,
     reweight: bool = False,
+    int8_qk: bool = False,
     sm_scale: Optional[float] = None,
     mask: Optional[np.ndarray] = None,
     info: Optional[dict] = None,
@@ -340,6 +424,8 @@ def forward_blocks(
     if reweight and "cbias" not in info:
         info["anchor"], info["ktilde"], info["vtilde"], info["cbias"] = reweight_summaries(
             q, k, v, prefix_len=prefix_len, sm_scale=sm_scale)
+    if int8_qk and "int8" not in info:
+        info["int8"] = int8_qk_codes(q, k)
     ksum = info["ktilde"] if reweight else info["kbar"]
     vsum = info["vtilde"] if reweight else info["vbar"]
     sel = info["sel"]
@@ -359,8 +445,19 @@ def forward_blocks(
             centroid=centroid,
             logmass=logmass,
             cbias_head=info["cbias"][b, h] if reweight else None,
+            int8_head=_int8_head(info["int8"], b, h, rows) if int8_qk else None,
         )
     return out, info
+
+
+def _int8_head(d, b, h, rows):
+    return dict(
+        qcode=d["qcode"][b, rows, h],
+        qscale=d["qscale"][b, rows, h],
+        kbase=d["kbase"][b, h],
+        kscale=d["kscale"][b, h],
+        kcode=d["kcode"][b, :, h],
+    )
 
 
 def forward(q, k, v, **kw):
