@@ -30,6 +30,7 @@ __all__ = [
     "SA_FLAG_LOGMASS",
     "SA_FLAG_EXACT_KV_ONLY",
     "SA_FLAG_REWEIGHT",
+    "SA_FLAG_INT8_QK",
 ]
 
 SA_ROUTE_TAU = 0
@@ -38,6 +39,7 @@ SA_FLAG_CENTROID = 1
 SA_FLAG_LOGMASS = 2
 SA_FLAG_EXACT_KV_ONLY = 4
 SA_FLAG_REWEIGHT = 8
+SA_FLAG_INT8_QK = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libsparse_attn.so"
@@ -84,6 +86,8 @@ class _Layout(ctypes.Structure):
         ("lists", ctypes.c_uint64),
         ("anchor", ctypes.c_uint64),
         ("cbias", ctypes.c_uint64),
+        ("k_int8", ctypes.c_uint64),
+        ("kbase", ctypes.c_uint64),
         ("n_blocks", ctypes.c_int32),
         ("n_blocks_padded", ctypes.c_int32),
         ("tail_rows", ctypes.c_int32),
@@ -184,6 +188,7 @@ class SparseAttnPlan:
         centroid: bool = True,
         logmass: bool = True,
         reweight: bool = False,
+        int8_qk: bool = False,
         sm_scale: Optional[float] = None,
         in_strides: Optional[Tuple[int, int, int]] = None,
         out_strides: Optional[Tuple[int, int, int]] = None,
@@ -205,7 +210,8 @@ class SparseAttnPlan:
         p.prefix_len = int(prefix_len)
         p.sm_scale = float(sm_scale) if sm_scale else 0.0
         p.flags = ((SA_FLAG_CENTROID if centroid else 0) | (SA_FLAG_LOGMASS if logmass else 0)
-                   | (SA_FLAG_EXACT_KV_ONLY if exact_kv_only else 0) | (SA_FLAG_REWEIGHT if reweight else 0))
+                   | (SA_FLAG_EXACT_KV_ONLY if exact_kv_only else 0) | (SA_FLAG_REWEIGHT if reweight else 0)
+                   | (SA_FLAG_INT8_QK if int8_qk else 0))
         handle = ctypes.c_void_p()
         _check(lib.sparse_attn_plan_create(ctypes.byref(p), ctypes.byref(handle)), "sparse_attn_plan_create")
         self._lib = lib
@@ -343,6 +349,20 @@ class SparseAttnPlan:
         nbp = self.layout["n_blocks_padded"]
         return self._view(ws, "anchor", torch.float32, (B, H, D)), self._view(ws, "cbias", torch.float32, (B, H, nbp))
 
+    def int8_views(self, ws):
+        """INT8 QK^T sections written by the pool step with ``int8_qk=True``:
+        residual codes int8 [B, H, n_b, 2, 32*D] (order in sparse_attn.h),
+        bf16 base rows [B, H, n_b, D] and fp32 block scales [B, H, n_b]."""
+        import torch
+
+        B, N, H, D = self.shape
+        nb = self.layout["n_blocks"]
+        codes = self._view(ws, "k_int8", torch.int8, (B, H, nb, 2, 32 * D))
+        rec = self._view(ws, "kbase", torch.int16, (B, H, nb, D + 8))
+        base = rec[..., :D].view(torch.bfloat16)
+        scale = rec[..., D : D + 2].contiguous().view(torch.float32)[..., 0]
+        return codes, base, scale
+
 
 def sparse_attn(
     q,
@@ -356,6 +376,7 @@ def sparse_attn(
     centroid: bool = True,
     logmass: bool = True,
     reweight: bool = False,
+    int8_qk: bool = False,
     sm_scale: Optional[float] = None,
     out=None,
     return_route: bool = False,
@@ -379,6 +400,7 @@ def sparse_attn(
         exact_kv_only=exact_kv_only,
         centroid=centroid,
         reweight=reweight,
+        int8_qk=int8_qk,
         logmass=logmass,
         sm_scale=sm_scale,
         in_strides=(q.stride(0), q.stride(1), q.stride(2)),

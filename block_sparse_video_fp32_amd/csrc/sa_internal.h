@@ -30,6 +30,7 @@ struct Shape {
   int reweight;             // Spark-Reweight centroids (never on the dense path)
   float scale;              // softmax scale
   int prefix_len;
+  int int8;                 // INT8 QK^T on the exact blocks
 };
 
 // Device workspace sections (see the layout notes in sparse_attn.h).
@@ -45,6 +46,8 @@ struct Workspace {
   int* lists;
   float* anchor;  // [B,H,D] reweight anchor
   float* cbias;   // [B,H,nbp] reweight centroid bias, log2 units
+  uint8_t* k8;     // [B,H,nb,2 half tiles] int8 residual codes, MFMA order
+  uint16_t* kbase; // [B,H,nb] records: bf16 base row (D), fp32 scale, zero (D + 8 slots)
 };
 
 hipError_t launch_pool_q(const Shape& s, const void* q, const Workspace& ws, hipStream_t stream);

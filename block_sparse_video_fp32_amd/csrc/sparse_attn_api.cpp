@@ -112,7 +112,8 @@ int validate_params(const sparse_attn_params& p) {
   if (!std::isfinite(p.sm_scale)) return fail(SA_EINVAL, "sm_scale must be finite");
   if ((p.flags & SA_FLAG_REWEIGHT) && !(p.flags & SA_FLAG_CENTROID))
     return fail(SA_EINVAL, "SA_FLAG_REWEIGHT needs SA_FLAG_CENTROID");
-  if (p.flags & ~(SA_FLAG_CENTROID | SA_FLAG_LOGMASS | SA_FLAG_EXACT_KV_ONLY | SA_FLAG_REWEIGHT))
+  if (p.flags &
+      ~(SA_FLAG_CENTROID | SA_FLAG_LOGMASS | SA_FLAG_EXACT_KV_ONLY | SA_FLAG_REWEIGHT | SA_FLAG_INT8_QK))
     return fail(SA_EINVAL, "unknown flag bits 0x%x", p.flags);
   return SA_OK;
 }
@@ -159,6 +160,7 @@ void build_plan(sparse_attn_plan* pl) {
   s.reweight = ((p.flags & SA_FLAG_REWEIGHT) && !s.dense) ? 1 : 0;
   s.scale = (float)scale;
   s.prefix_len = p.prefix_len;
+  s.int8 = (p.flags & SA_FLAG_INT8_QK) ? 1 : 0;
 
   sparse_attn_ws_layout& L = pl->layout;
   std::memset(&L, 0, sizeof(L));
@@ -178,6 +180,8 @@ void build_plan(sparse_attn_plan* pl) {
   L.lists = off; off = align256(off + bh * s.nb * (uint64_t)s.nb * sizeof(int32_t));
   L.anchor = off; off = align256(off + bh * p.D * sizeof(float));
   L.cbias = off; off = align256(off + bh * s.nbp * sizeof(float));
+  L.k_int8 = off; off = align256(off + (s.int8 ? bh * s.nb * 64ull * p.D : 0));
+  L.kbase = off; off = align256(off + (s.int8 ? bh * s.nb * (uint64_t)(p.D + 8) * sizeof(uint16_t) : 0));
   L.total_bytes = off;
   L.n_blocks = s.nb;
   L.n_blocks_padded = s.nbp;
@@ -202,6 +206,8 @@ sa::Workspace carve(const sparse_attn_plan* pl, void* ws) {
   w.lists = reinterpret_cast<int*>(base + L.lists);
   w.anchor = reinterpret_cast<float*>(base + L.anchor);
   w.cbias = reinterpret_cast<float*>(base + L.cbias);
+  w.k8 = reinterpret_cast<uint8_t*>(base + L.k_int8);
+  w.kbase = reinterpret_cast<uint16_t*>(base + L.kbase);
   return w;
 }
 

@@ -215,6 +215,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
   __shared__ float al[D];   // reweight anchor
   __shared__ float wl[64];  // reweight row weights
   __shared__ float red[8];
+  __shared__ float kbl[D];  // INT8 QK^T base row (bf16 values)
 
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const long long bh = (long long)b * s.H + h;
@@ -312,6 +313,11 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
       ws.kbar[(bh * s.nb + j) * D + d] = mean;
       kc[kc_index(d)] = (uint16_t)f32_to_bf16_bits(cval);
       kdot = al[d] * wsum;
+      if (s.int8) {
+        const uint32_t bb = f32_to_bf16_bits(mean);
+        ws.kbase[(bh * s.nb + j) * (D + 8) + d] = (uint16_t)bb;
+        kbl[d] = bf16_bits_to_f32(bb);
+      }
     } else {
       ws.vbar[(bh * s.nb + j) * D + d] = mean;
       vc[vc_index(d)] = (uint16_t)f32_to_bf16_bits(cval);
@@ -331,13 +337,49 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
     }
   }
 
+  // INT8 QK^T (thakicloud accel-stack post, measured results): residual
+  // codes of the keys about the bf16 base row, one scale per block, in the
+  // A-operand order of v_mfma_i32_32x32x32_i8; the bf16 K tiles are not
+  // needed then.
+  if (s.int8) {
+    __syncthreads();
+    float mx = 0.0f;
+    for (int e = tid; e < n * D; e += 256) {
+      const int row = e / D, d = e % D;
+      mx = fmaxf(mx, fabsf(bf16_bits_to_f32(Kl[row * LS + d]) - kbl[d]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = mx;
+    __syncthreads();
+    const float sc = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])) / 127.0f;
+    uint16_t* rec = ws.kbase + (bh * s.nb + j) * (D + 8);
+    if (tid == 0) *reinterpret_cast<uint4*>(rec + D) = make_uint4(__float_as_uint(sc), 0u, 0u, 0u);
+    uint8_t* k8 = ws.k8 + (bh * s.nb + j) * (64LL * D);
+    for (int o = tid; o < 4 * D; o += 256) {  // 16-byte chunks, 2 * (D/32) * 64 of them
+      const int ht = o / (2 * D), t = (o / 64) % (D / 32), l = o % 64;
+      const int row = 32 * ht + kappa(l & 31);
+      uint32_t wd[4] = {0u, 0u, 0u, 0u};
+      if (row < n && sc > 0.0f) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int d = 32 * t + 16 * (jj >> 3) + 8 * (l >> 5) + (jj & 7);
+          const float x = bf16_bits_to_f32(Kl[row * LS + d]) - kbl[d];
+          const int code = (int)fminf(fmaxf(rintf(x / sc), -127.0f), 127.0f);
+          wd[jj >> 2] |= ((uint32_t)code & 0xffu) << (8 * (jj & 3));
+        }
+      }
+      *reinterpret_cast<uint4*>(k8 + (long long)o * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+  }
+
   uint16_t* kp = ws.kp + (bh * s.nb + j) * (2LL * HT);
   uint16_t* vp = ws.vp + (bh * s.nb + j) * (2LL * HT);
 #pragma unroll
   for (int i = 0; i < CPR / 4; ++i) {
     const int o = tid + 256 * i;  // output 16-byte chunk, 64 * CPR of them
     const int ht = o / (64 * (D / 16)), m = (o / 64) % (D / 16), l = o % 64;
-    {
+    if (!s.int8) {
       // K: chunk (m, l) = K[kappa(l % 32)][16 m + 8 (l / 32) .. +8]
       const int row = 32 * ht + kappa(l & 31);
       const int d0 = 16 * m + 8 * (l >> 5);
@@ -563,6 +605,8 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
 // ---------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // s_waitcnt immediate: vmcnt(n) and lgkmcnt(0), expcnt untouched.
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
@@ -611,6 +655,61 @@ __device__ __forceinline__ void copy_blocks(const uint16_t* src, const int (&dof
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* stage, int blk, int lane) {
   return *reinterpret_cast<const bf16x8*>(stage + blk * 1024 + lane * 16);
+}
+
+// One global -> LDS copy of this lane's 16 bytes at src to dst + 16 * lane
+// (same instruction and M0 handling as copy_blocks).
+__device__ __forceinline__ void copy_one(const void* src, uint32_t dst) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(dst)
+      : "memory");
+}
+
+// INT8 QK^T of one half tile: S^T = R8 Q8^T on v_mfma_i32_32x32x32_i8 (exact
+// int32 sums), returned as fp32.  Step t pairs byte j of lane l of the code
+// block with byte j of lane l of q8[t]: both hold dimension
+// 32 t + 16 (j/8) + 8 (l/32) + j % 8.
+template <int NT>
+__device__ __forceinline__ f32x16 tile_qk_i8(const uint8_t* stage, int lane, const i32x4 (&q8)[NT]) {
+  i32x4 kf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) kf[t] = *reinterpret_cast<const i32x4*>(stage + t * 1024 + lane * 16);
+  i32x16 iacc = {};
+#pragma unroll
+  for (int t = 0; t < NT; ++t) iacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t], q8[t], iacc, 0, 0, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
+  f32x16 sacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sacc[i] = (float)iacc[i];
+  return sacc;
+}
+
+// q . base_c of this lane's query row against the bf16 base row at rec: each
+// half of the wave holds the dimensions of its own Q fragments, the two
+// partial sums are added across the halves.
+template <int NK>
+__device__ __forceinline__ float mean_dot(const uint8_t* rec, int hh, const bf16x8 (&qf)[NK]) {
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const uint4 bw = *reinterpret_cast<const uint4*>(rec + (16 * k + 8 * hh) * 2);
+    const uint4 qw = __builtin_bit_cast(uint4, qf[k]);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, bw.x), __builtin_bit_cast(bf16x2, qw.x), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, bw.y), __builtin_bit_cast(bf16x2, qw.y), a1, false);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, bw.z), __builtin_bit_cast(bf16x2, qw.z), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, bw.w), __builtin_bit_cast(bf16x2, qw.w), a1, false);
+  }
+  const float part = a0 + a1;
+  const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+  return __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
 }
 
 // S^T (32 keys x this wave's 32 queries) of the half tile in `stage`.
@@ -672,24 +771,27 @@ __device__ __forceinline__ void tile_key_bias_rw(float (&kb)[16], int c, int nb,
 }
 
 // Maximum logit of this lane's query over one half tile.
-__device__ __forceinline__ float tile_row_max(const f32x16& sacc, const float (&kb)[16], float c1) {
+__device__ __forceinline__ float tile_row_max(const f32x16& sacc, const float (&kb)[16], float a) {
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) m = fmaxf(m, fmaf(sacc[i], c1, kb[i]));
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fmaf(sacc[i], a, kb[i]));
   const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
   return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 
-// P = exp2(S^T c1 + kb - mref) in bf16, row sums, O^T += V^T P^T.
+// P = exp2(S^T a + kb - mref) in bf16 (kb replaced by the lane constant boff
+// on plain tiles), row sums, O^T += V^T P^T.  V^T starts at block vblk of the
+// stage.
 template <int NK, bool PLAIN>
-__device__ __forceinline__ void tile_pv(const uint8_t* stage, int lane, const f32x16& sacc, const float (&kb)[16],
-                                        float c1, float mref, f32x16 (&acc)[NK / 2], float (&lsum)[2]) {
+__device__ __forceinline__ void tile_pv(const uint8_t* stage, int vblk, int lane, const f32x16& sacc,
+                                        const float (&kb)[16], float a, float boff, float mref,
+                                        f32x16 (&acc)[NK / 2], float (&lsum)[2]) {
   bf16x8 vf[NK];
 #pragma unroll
-  for (int k = 0; k < NK; ++k) vf[k] = lds_frag(stage, NK + k, lane);
+  for (int k = 0; k < NK; ++k) vf[k] = lds_frag(stage, vblk + k, lane);
   float pe[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) pe[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c1, (PLAIN ? 0.0f : kb[i]) - mref));
+  for (int i = 0; i < 16; ++i) pe[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], a, (PLAIN ? boff : kb[i]) - mref));
   bf16x8 pb[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -718,7 +820,7 @@ __device__ __forceinline__ void tile_pv(const uint8_t* stage, int lane, const f3
   __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
 }
 
-template <int D, int S, bool RW>
+template <int D, int S, bool RW, bool Q8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attend_kernel(
     Shape s, const uint16_t* __restrict__ q, uint16_t* __restrict__ out, Workspace ws) {
   constexpr int NK = D / 16;          // QK k-steps = K blocks = PV MFMAs per tile
@@ -728,6 +830,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   constexpr int HT = 32 * D;          // elements of a half tile
   constexpr int STAGE = NBLK * 1024;  // bytes of one ring stage
   constexpr int NW = SA_MAX_BLOCKS / 32;
+  constexpr int NT = D / 32;          // INT8 QK k-steps
+  static_assert(!Q8 || S == 2, "INT8 copies are not balanced across waves: every ring step waits for all");
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // S * STAGE bytes
   __shared__ uint32_t sel[2][NW];            // selected key blocks of a0, a1
   __shared__ uint16_t ulist[SA_MAX_BLOCKS];  // union of the two lists
@@ -763,6 +867,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       uint4 v4 = make_uint4(0, 0, 0, 0);
       if (exists && qrow < N) v4 = *reinterpret_cast<const uint4*>(qp + 16 * k);
       qf[k] = __builtin_bit_cast(bf16x8, v4);
+    }
+  }
+  // INT8 QK^T: the row's scale s_q = max |q| / 127 and its codes, in the
+  // B-operand order of the int8 MFMA (bytes 0..7 of step t from qf[2t],
+  // bytes 8..15 from qf[2t + 1]).
+  i32x4 q8[Q8 ? NT : 1];
+  float sq = 0.0f;
+  if constexpr (Q8) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qf[k][e]));
+    const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+    amax = fmaxf(__uint_as_float(pm[0]), __uint_as_float(pm[1]));
+    sq = amax / 127.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const float xq = (float)qf[2 * t + (jj >> 3)][jj & 7];
+        const int code = sq > 0.0f ? (int)fminf(fmaxf(rintf(xq / sq), -127.0f), 127.0f) : 0;
+        wd[jj >> 2] |= ((uint32_t)code & 0xffu) << (8 * (jj & 3));
+      }
+      q8[t] = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
     }
   }
 
@@ -911,8 +1041,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     if (v >= tab_base + 64) tab_load(v & ~63);
     return __builtin_amdgcn_readlane(tabv, v - tab_base);
   };
+  // INT8 exact half tile: 1 KB blocks [codes 0 .. NT-1 | V^T 0 .. NK-1 |
+  // base record], block i copied by wave i % 4.
+  const uint8_t* k8_bh = ws.k8 + bh * nb * 64LL * D;
+  const uint16_t* vp_bh = ws.vp + bh * nb * 2LL * HT;
+  const uint16_t* kr_bh = ws.kbase + bh * nb * (long long)(D + 8);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+  auto copy_q8 = [&](int c, int ht, int stg) {
+    const uint32_t base = ring_lds + stg * STAGE;
+#pragma unroll
+    for (int i = 0; i < (NT + NK + 4) / 4; ++i) {
+      const int bi = w + 4 * i;
+      if (bi < NT)
+        copy_one(k8_bh + (2LL * c + ht) * 32 * D + bi * 1024 + lane * 16, base + bi * 1024);
+      else if (bi < NT + NK)
+        copy_one(vp_bh + (2LL * c + ht) * HT + (bi - NT) * 512 + lane * 8, base + bi * 1024);
+      else if (bi == NT + NK && lane <= D / 8)
+        copy_one(kr_bh + (long long)c * (D + 8) + lane * 8, base + bi * 1024);
+    }
+  };
   auto copy_tile = [&](int v, int e, int stg) {
     const int c = e & 0xfff;
+    if constexpr (Q8) {
+      if (v < TE) {
+        copy_q8(c, v & 1, stg);
+        return;
+      }
+    }
     const long long off = (v >= TE) ? (long long)c * HT : ((long long)c * 2 + (v & 1)) * HT;
     copy_blocks<PER>(((v >= TE) ? ce_bh : ex_bh) + off, doff, my_dst + stg * STAGE);
   };
@@ -949,6 +1104,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                     bias_tail);
   };
 
+  // Scores of a half tile.  The logit (log2 units) is sacc * ta + tb plus the
+  // per-key term; bf16 QK^T gives ta = c1, tb = 0.  INT8 exact tiles give
+  // ta = c1 s_q s_c and tb = c1 q . base_c, taken at the block's first half
+  // tile from the base record that follows V^T in the stage.
+  float ta = c1, tb = 0.0f;
+  int vblk = NK;  // first V^T block of the stage
+  auto qk = [&](int u, const uint8_t* stage) -> f32x16 {
+    if constexpr (Q8) {
+      if (u < TE) {
+        const uint8_t* rec = stage + (NT + NK) * 1024;
+        if (!(u & 1)) {
+          ta = c1 * (sq * *reinterpret_cast<const float*>(rec + 2 * D));
+          tb = c1 * mean_dot<NK>(rec, hh, qf);
+        }
+        vblk = NT;
+        return tile_qk_i8<NT>(stage, lane, q8);
+      }
+      ta = c1;
+      tb = 0.0f;
+      vblk = NK;
+    }
+    return tile_qk<NK>(stage, lane, qf);
+  };
+  auto bias_t = [&](int u, int eu, float (&kb)[16]) {
+    bias_of(u, eu, kb);
+    if constexpr (Q8) {
+      if (u < TE)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kb[i] += tb;
+    }
+  };
+
   // Q and the lists are in registers / LDS before the first copy is issued.
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   for (int attempt = 0; attempt < 2 && TU > 0; ++attempt) {
@@ -958,10 +1145,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       for (int u = 0; u < TU; ++u) {
         const int eu = ring_step(u);
         if ((eu >> 12) & myflag) {
-          const f32x16 sacc = tile_qk<NK>(rd + st * STAGE, lane, qf);
+          const f32x16 sacc = qk(u, rd + st * STAGE);
           float kb[16];
-          bias_of(u, eu, kb);
-          mmax = fmaxf(mmax, tile_row_max(sacc, kb, c1));
+          bias_t(u, eu, kb);
+          mmax = fmaxf(mmax, tile_row_max(sacc, kb, ta));
         }
         ring_next();
       }
@@ -982,14 +1169,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     if (u < TU) {
       const int eu = ring_step(u);
       const uint8_t* stage = rd + st * STAGE;
-      const f32x16 sacc = tile_qk<NK>(stage, lane, qf);
+      const f32x16 sacc = qk(u, stage);
       float kb[16];
-      bias_of(u, eu, kb);
+      bias_t(u, eu, kb);
       if (!safe) {
-        const float m = tile_row_max(sacc, kb, c1);
+        const float m = tile_row_max(sacc, kb, ta);
         mref = (m == -INFINITY) ? 0.0f : m + 32.0f;
       }
-      tile_pv<NK, false>(stage, lane, sacc, kb, c1, mref, acc, lsum);
+      tile_pv<NK, false>(stage, vblk, lane, sacc, kb, ta, 0.0f, mref, acc, lsum);
       ring_next();
       ++u;
     }
@@ -997,11 +1184,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       const int eu = ring_step(u);
       if ((eu >> 12) & myflag) {
         const uint8_t* stage = rd + st * STAGE;
-        const f32x16 sacc = tile_qk<NK>(stage, lane, qf);
+        const f32x16 sacc = qk(u, stage);
         float kb[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) kb[i] = 0.0f;
-        tile_pv<NK, true>(stage, lane, sacc, kb, c1, mref, acc, lsum);
+        tile_pv<NK, true>(stage, vblk, lane, sacc, kb, ta, tb, mref, acc, lsum);
       }
       ring_next();
     }
@@ -1009,10 +1196,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       const int eu = ring_step(u);
       if ((eu >> 12) & myflag) {
         const uint8_t* stage = rd + st * STAGE;
-        const f32x16 sacc = tile_qk<NK>(stage, lane, qf);
+        const f32x16 sacc = qk(u, stage);
         float kb[16];
-        bias_of(u, eu, kb);
-        tile_pv<NK, false>(stage, lane, sacc, kb, c1, mref, acc, lsum);
+        bias_t(u, eu, kb);
+        tile_pv<NK, false>(stage, vblk, lane, sacc, kb, ta, 0.0f, mref, acc, lsum);
       }
       ring_next();
     }
@@ -1051,16 +1238,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // CU, which is 6-9% faster than two.
 constexpr int kAttendStages = 2;
 
-template <int D, int S, bool RW>
+template <int D, int S, bool RW, bool Q8>
 hipError_t launch_attend_t(const Shape& s, const uint16_t* q, uint16_t* out, const Workspace& ws,
                            hipStream_t stream) {
   constexpr int bytes = S * (D / 8) * 1024;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, S, RW>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, S, RW, Q8>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((long long)s.B * s.H * ((s.nb + 1) / 2)));
-  hipLaunchKernelGGL((attend_kernel<D, S, RW>), grid, dim3(256), bytes, stream, s, q, out, ws);
+  hipLaunchKernelGGL((attend_kernel<D, S, RW, Q8>), grid, dim3(256), bytes, stream, s, q, out, ws);
   return hipGetLastError();
+}
+
+template <int D, bool RW>
+hipError_t launch_attend_d(const Shape& s, const uint16_t* q, uint16_t* out, const Workspace& ws,
+                           hipStream_t stream) {
+  if (s.int8) return launch_attend_t<D, kAttendStages, RW, true>(s, q, out, ws, stream);
+  return launch_attend_t<D, kAttendStages, RW, false>(s, q, out, ws, stream);
 }
 
 template <int D>
@@ -1118,14 +1312,14 @@ hipError_t launch_select(const Shape& s, const Workspace& ws, hipStream_t stream
 hipError_t launch_attend(const Shape& s, const void* q, void* out, const Workspace& ws, hipStream_t stream) {
   const auto* qq = static_cast<const uint16_t*>(q);
   auto* oo = static_cast<uint16_t*>(out);
-  // Reweight mode is its own instantiation, so that the default kernel
-  // carries none of its registers or LDS.
+  // Reweight and INT8 QK^T are instantiations of their own, so that the
+  // default kernel carries none of their registers or LDS.
   if (s.reweight) {
-    if (s.D == 128) return launch_attend_t<128, kAttendStages, true>(s, qq, oo, ws, stream);
-    return launch_attend_t<64, kAttendStages, true>(s, qq, oo, ws, stream);
+    if (s.D == 128) return launch_attend_d<128, true>(s, qq, oo, ws, stream);
+    return launch_attend_d<64, true>(s, qq, oo, ws, stream);
   }
-  if (s.D == 128) return launch_attend_t<128, kAttendStages, false>(s, qq, oo, ws, stream);
-  return launch_attend_t<64, kAttendStages, false>(s, qq, oo, ws, stream);
+  if (s.D == 128) return launch_attend_d<128, false>(s, qq, oo, ws, stream);
+  return launch_attend_d<64, false>(s, qq, oo, ws, stream);
 }
 
 }  // namespace sa

@@ -52,7 +52,7 @@ extern "C" {
 
 #define SA_BLOCK 64          /* rows per query / key block */
 #define SA_MAX_BLOCKS 2048   /* largest supported n_b = ceil(N / 64) */
-#define SA_ABI_VERSION 3
+#define SA_ABI_VERSION 4
 
 /* Routing modes (sparse_attn_params.route). */
 #define SA_ROUTE_TAU 0   /* S >= mean + tau * std; tau = -inf is the dense path */
@@ -77,6 +77,15 @@ extern "C" {
  * bias = logsumexp(x) - anchor . Ktilde * scale, used in place of log(n_c).
  * Requires SA_FLAG_CENTROID; routing still uses the block means. */
 #define SA_FLAG_REWEIGHT 8u
+/* INT8 QK^T on the exact blocks (thakicloud "MiniMax-H3 ComfyUI accel
+ * stack" post, section on measured results: only each key block's residual
+ * about its mean is quantised, the mean term stays bf16).  Reading:
+ * base_c = bf16(fp32 mean of the block's keys); one scale per key block
+ * s_c = max |k - base_c| / 127 over its valid rows; one scale per query row
+ * s_q = max_d |q| / 127; codes rint(x / s) clipped to +-127, decided in fp32;
+ * exact logit = scale * (q . base_c + s_q s_c (q8 . r8)).  Centroid logits
+ * and P V are unchanged.  Without it (the default) QK^T is bf16. */
+#define SA_FLAG_INT8_QK 16u
 #define SA_FLAGS_DEFAULT (SA_FLAG_CENTROID | SA_FLAG_LOGMASS)
 
 /* Error codes. */
@@ -106,7 +115,8 @@ typedef struct sparse_attn_params {
 
 typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
 
-/* Byte offsets of the workspace sections (all 256-byte aligned).
+/* Byte offsets of the workspace sections (all 256-byte aligned; a section
+ * a plan does not use has size 0).
  *
  * After sparse_attn_pool:
  *   qbar, kbar, vbar  fp32 [B, H, n_b, D]: the block means of Q, K, V.
@@ -129,6 +139,14 @@ typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
  *                     SA_FLAG_REWEIGHT, off the dense path).
  *   cbias             fp32 [B, H, n_bp]: the reweight centroid bias of each
  *                     block in log2 units (bias / ln 2); same condition.
+ *   k_int8            int8, with SA_FLAG_INT8_QK only: per (b, h, block) two
+ *                     half tiles of residual codes (zero past N); in a half
+ *                     tile, byte ((t*64 + l)*16 + j) holds the code of
+ *                     K[kappa(l % 32)][32 t + 16 (j/8) + 8 (l/32) + j % 8],
+ *                     t < D/32 (the A operand of v_mfma_i32_32x32x32_i8).
+ *   kbase             with SA_FLAG_INT8_QK only: per (b, h, block) a record
+ *                     of D + 8 16-bit slots: the bf16 base row base_c, then
+ *                     the fp32 block scale s_c in slots D, D + 1, then zero.
  * After sparse_attn_select:
  *   counts            int32 [B, H, n_b]: selected key blocks per query block.
  *   lists             int32 [B, H, n_b, n_b]: the selected key blocks in
@@ -141,6 +159,7 @@ typedef struct sparse_attn_ws_layout {
   uint64_t kbar_packed, vbar_packed;
   uint64_t counts, lists;
   uint64_t anchor, cbias;
+  uint64_t k_int8, kbase;
   int32_t n_blocks;        /* n_b */
   int32_t n_blocks_padded; /* n_bp */
   int32_t tail_rows;       /* valid rows of block n_b - 1 */

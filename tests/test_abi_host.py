@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.sparse_attn_abi_version() == 3
+    assert lib.sparse_attn_abi_version() == 4
 
 
 def _params(**kw):
@@ -84,7 +84,7 @@ def _create(lib, p):
         (dict(prefix_len=1025), SA_EINVAL),
         (dict(prefix_len=1024), 0),
         (dict(sm_scale=float("inf")), SA_EINVAL),
-        (dict(flags=16), SA_EINVAL),
+        (dict(flags=32), SA_EINVAL),
         (dict(in_stride_b=3 * 1024 * 128, in_stride_t=3 * 128, in_stride_h=64), 0),
         (dict(in_stride_b=1024 * 128, in_stride_t=130, in_stride_h=64), SA_EALIGN),
         (dict(in_stride_b=0, in_stride_t=128, in_stride_h=64), SA_EINVAL),
@@ -108,22 +108,27 @@ def test_null_arguments(lib):
     lib.sparse_attn_plan_destroy(None)
 
 
-def test_workspace_layout_matches_documented_sizes():
-    plan = binding.SparseAttnPlan(2, 1000, 3, 128, tau=1.0, prefix_len=70)
+@pytest.mark.parametrize("int8_qk", [False, True])
+def test_workspace_layout_matches_documented_sizes(int8_qk):
+    plan = binding.SparseAttnPlan(2, 1000, 3, 128, tau=1.0, prefix_len=70, int8_qk=int8_qk)
     L = plan.layout
     nb = 16
     assert L["n_blocks"] == nb and L["n_blocks_padded"] == 64
     assert L["tail_rows"] == 1000 - 64 * 15 and L["prefix_blocks"] == 2 and L["dense"] == 0
     names = ("qbar", "kbar", "vbar", "k_packed", "v_packed", "kbar_packed", "vbar_packed", "counts", "lists",
-             "anchor", "cbias")
+             "anchor", "cbias", "k_int8", "kbase")
     offs = sorted((L[n], n) for n in names)
     sizes = dict(qbar=2 * 3 * nb * 128 * 4, kbar=2 * 3 * nb * 128 * 4, vbar=2 * 3 * nb * 128 * 4,
                  k_packed=2 * 3 * nb * 64 * 128 * 2, v_packed=2 * 3 * nb * 64 * 128 * 2,
                  kbar_packed=2 * 3 * 64 * 128 * 2, vbar_packed=2 * 3 * 64 * 128 * 2,
-                 counts=2 * 3 * nb * 4, lists=2 * 3 * nb * nb * 4, anchor=2 * 3 * 128 * 4, cbias=2 * 3 * 64 * 4)
+                 counts=2 * 3 * nb * 4, lists=2 * 3 * nb * nb * 4, anchor=2 * 3 * 128 * 4, cbias=2 * 3 * 64 * 4,
+                 k_int8=2 * 3 * nb * 64 * 128 if int8_qk else 0,
+                 kbase=2 * 3 * nb * (128 + 8) * 2 if int8_qk else 0)
     for (o, n), (o2, _) in zip(offs, offs[1:] + [(L["total_bytes"], "end")]):
         assert o % 256 == 0
         assert o2 - o >= sizes[n]
+    if not int8_qk:
+        assert L["kbase"] == L["k_int8"]  # empty sections
 
 
 @pytest.mark.parametrize("ratio,nb,k", [(0.1, 598, 60), (0.1, 640, 64), (0.2, 512, 103), (1.0, 17, 17), (1e-9, 100, 1)])
@@ -191,3 +196,11 @@ def test_reweight_flag_needs_centroids(lib):
     assert _create(lib, _params(flags=3 | SA_FLAG_REWEIGHT)) == 0
     assert _create(lib, _params(flags=2 | SA_FLAG_REWEIGHT)) == SA_EINVAL  # centroids off
     assert "SA_FLAG_CENTROID" in lib.sparse_attn_last_error().decode()
+
+
+def test_int8_flag_is_accepted(lib):
+    from block_sparse_video_fp32_amd.binding import SA_FLAG_INT8_QK
+    assert SA_FLAG_INT8_QK == 16
+    for f in (3, 0, 3 | 8, 3 | 4):
+        assert _create(lib, _params(flags=f | SA_FLAG_INT8_QK)) == 0
+    assert _create(lib, _params(flags=32)) == SA_EINVAL

@@ -115,8 +115,8 @@ def check_output(got, ref, label=""):
 
 
 def oracle_kw(kw):
-    o = {k: kw[k] for k in ("tau", "topk_ratio", "prefix_len", "centroid", "logmass", "reweight", "sm_scale")
-         if k in kw}
+    o = {k: kw[k] for k in ("tau", "topk_ratio", "prefix_len", "centroid", "logmass", "reweight", "int8_qk",
+                            "sm_scale") if k in kw}
     if kw.get("exact_kv_only"):
         o["prefix_rows"] = False  # exact_kv: the sink without dense prefix rows
     return o
@@ -233,6 +233,39 @@ def test_reweight_summaries(N, D, prefix_len):
             assert (ck[nb:] == 0).all() and (cv[nb:] == 0).all()
 
 
+def _unpack_k8(tile, D):
+    """Packed INT8 residual half tile (32*D,) -> [32, D] per sparse_attn.h:
+    byte ((t*64 + l)*16 + j) is the code of
+    K[kappa(l % 32)][32 t + 16 (j // 8) + 8 (l // 32) + j % 8]."""
+    t = tile.reshape(D // 32, 2, 32, 2, 8)  # [t, l // 32, l % 32, j // 8, j % 8]
+    k = np.empty((32, D), dtype=tile.dtype)
+    for r in range(32):
+        k[_kappa(r)] = t[:, :, r].transpose(0, 2, 1, 3).reshape(D)
+    return k
+
+
+@pytest.mark.parametrize("N,D", [(1100, 64), (1024, 128), (200, 128)])
+def test_int8_codes_match_oracle(N, D):
+    """Residual codes, bf16 base rows and block scales are decided in fp32 on
+    both sides: they must be bit-identical to the oracle's."""
+    q, k, v = inputs.clustered(2, N, 2, D, seed=N + 7) if N >= 256 else inputs.iid(2, N, 2, D, seed=N + 7)
+    run = GpuRun(q, k, v, tau=1.0, int8_qk=True)
+    want = O.int8_qk_codes(_f32(q), _f32(k))
+    codes, base, scale = (t.cpu() for t in run.plan.int8_views(run.ws))
+    np.testing.assert_array_equal(base.float().numpy(), want["kbase"])
+    np.testing.assert_array_equal(scale.numpy(), want["kscale"])
+    codes = codes.numpy()
+    nb = O.num_blocks(N)
+    kc = np.zeros((2, nb * 64, 2, D), dtype=np.int8)
+    kc[:, :N] = want["kcode"]
+    for b in range(2):
+        for h in range(2):
+            for c in range(nb):
+                for ht in range(2):
+                    rows = slice(64 * c + 32 * ht, 64 * c + 32 * ht + 32)
+                    np.testing.assert_array_equal(_unpack_k8(codes[b, h, c, ht], D), kc[b, rows, h])
+
+
 # ---------------------------------------------------- small, every output row
 
 
@@ -253,6 +286,12 @@ SMALL = [
     ("reweight_exact_kv", dict(B=1, N=1000, H=3, D=64), dict(tau=0.5, prefix_len=70, exact_kv_only=True,
                                                               reweight=True)),
     ("reweight_dense", dict(B=1, N=777, H=2, D=128), dict(tau=-math.inf, reweight=True)),
+    ("int8_tau", dict(B=1, N=1024, H=2, D=128), dict(tau=1.0, int8_qk=True)),
+    ("int8_prefix_tail_d64", dict(B=2, N=1100, H=2, D=64), dict(tau=1.0, prefix_len=100, int8_qk=True)),
+    ("int8_topk_reweight", dict(B=1, N=1500, H=2, D=128), dict(topk_ratio=0.25, prefix_len=128, reweight=True,
+                                                                int8_qk=True)),
+    ("int8_exact_kv", dict(B=1, N=1000, H=3, D=64), dict(tau=0.5, prefix_len=70, exact_kv_only=True, int8_qk=True)),
+    ("int8_dense_tail", dict(B=1, N=777, H=2, D=128), dict(tau=-math.inf, int8_qk=True)),
     ("no_centroid", dict(B=1, N=1024, H=2, D=128), dict(tau=1.0, centroid=False)),
     ("no_logmass", dict(B=1, N=1024, H=2, D=64), dict(tau=1.0, logmass=False)),
     ("scale", dict(B=1, N=512, H=2, D=64), dict(tau=0.5, sm_scale=0.3)),
@@ -294,10 +333,11 @@ def _spike_inputs(N, H, D, spike_block, seed):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("tau", [1.0, -math.inf], ids=["tau1", "dense"])
-def test_logit_spike_recompute(D, tau):
+@pytest.mark.parametrize("tau,int8_qk", [(1.0, False), (-math.inf, False), (1.0, True)],
+                         ids=["tau1", "dense", "tau1_int8"])
+def test_logit_spike_recompute(D, tau, int8_qk):
     q, k, v = _spike_inputs(N=650, H=2, D=D, spike_block=5, seed=D)
-    full_parity(q, k, v, tau=tau)
+    full_parity(q, k, v, tau=tau, int8_qk=int8_qk)
 
 
 def test_tiny_matches_oracle_lists_exactly():
@@ -380,9 +420,11 @@ def test_max_blocks():
 # -------------------------------------------- the benchmarked workloads
 
 
-def _sampled_parity(name, n_sample=48, **over):
+def _sampled_parity(name, n_sample=48, int8_qk=False, **over):
     w = inputs.make_workload(name, **over)
     kw = dict(tau=w.tau, topk_ratio=w.topk_ratio, prefix_len=w.prefix_len)
+    if int8_qk:
+        kw["int8_qk"] = True
     if w.topk_ratio is not None:
         kw.pop("tau")
     else:
@@ -432,3 +474,7 @@ def test_workload_n32k_sampled():
 
 def test_workload_h3_sampled():
     _sampled_parity("h3")
+
+
+def test_workload_n32k_int8_sampled():
+    _sampled_parity("n32k", n_sample=24, int8_qk=True)
