@@ -129,6 +129,7 @@ def main():
     ap.add_argument("--workload", default="n32k", choices=["tiny", "n4k", "n16k", "n32k", "h3"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-modes", action="store_true", help="skip the reweight and INT8 QK^T timings")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 256 MiB device copy before the steps (scales rocprofv3 byte counters)")
@@ -222,6 +223,40 @@ def main():
         dense_ms = s0.elapsed_time(s1) / kd
         print(f"# dense: {dense_ms:.3f} ms/call", file=sys.stderr, flush=True)
 
+    # optional modes of the same call on the same inputs: Spark-Reweight
+    # centroids and INT8 QK^T on the exact blocks (same routing)
+    modes = None
+    if not args.no_modes:
+        modes = {}
+        for name, extra in (("reweight", dict(reweight=True)), ("int8_qk", dict(int8_qk=True))):
+            mplan = binding.SparseAttnPlan(B, N, H, D, prefix_len=w.prefix_len, **rkw, **extra)
+            mws = mplan.workspace(dev)
+            for _ in range(2):
+                mplan.pool(q, k, v, mws)
+                mplan.select(mws)
+                mplan.attend(q, out, mws)
+            torch.cuda.synchronize()
+            km = max(3, K // 2)
+            me = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(km)]
+            for i in range(km):
+                me[i][0].record(stream)
+                mplan.pool(q, k, v, mws)
+                me[i][1].record(stream)
+                mplan.select(mws)
+                me[i][2].record(stream)
+                mplan.attend(q, out, mws)
+                me[i][3].record(stream)
+            torch.cuda.synchronize()
+            m_call = sum(e[0].elapsed_time(e[3]) for e in me) / km
+            m_pool = sum(e[0].elapsed_time(e[1]) for e in me) / km
+            m_att = sum(e[2].elapsed_time(e[3]) for e in me) / km
+            modes[name] = {"ms_per_call": round(m_call, 4), "pool_ms": round(m_pool, 4), "attend_ms": round(m_att, 4),
+                           "attend_vs_default": round(t_att / m_att, 3)}
+            print(f"# {name}: {m_call:.3f} ms/call (pool {m_pool:.3f}, attend {m_att:.3f})", file=sys.stderr,
+                  flush=True)
+            del mws, mplan
+        torch.cuda.empty_cache()
+
     dense_flops = 4.0 * B * H * N * N * D
     # pool = pool_q (reads Q, writes Qbar) + pack_kv (reads K, V; writes Kbar,
     # Vbar, the packed K and V^T tiles and the packed bf16 centroids)
@@ -258,6 +293,7 @@ def main():
         "dense_equivalent_tflops": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
         "own_dense_tflops": None if dense_ms is None else round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
         "kernels_ms": {"pool": round(t_pool, 4), "select": round(t_sel, 4), "attend": round(t_att, 4)},
+        "modes": modes,
         "pool_gbs": round(pool_bytes / (t_pool * 1e-3) / 1e9, 1),
         "select_gbs": round(sel_bytes / (t_sel * 1e-3) / 1e9, 1),
         "roofline": {

@@ -712,13 +712,15 @@ __device__ __forceinline__ float mean_dot(const uint8_t* rec, int hh, const bf16
   return __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
 }
 
-// S^T (32 keys x this wave's 32 queries) of the half tile in `stage`.
+// S^T (32 keys x this wave's 32 queries) of the half tile in `stage`, added
+// to init.
 template <int NK>
-__device__ __forceinline__ f32x16 tile_qk(const uint8_t* stage, int lane, const bf16x8 (&qf)[NK]) {
+__device__ __forceinline__ f32x16 tile_qk(const uint8_t* stage, int lane, const bf16x8 (&qf)[NK],
+                                          const f32x16& init) {
   bf16x8 kf[NK];
 #pragma unroll
   for (int k = 0; k < NK; ++k) kf[k] = lds_frag(stage, k, lane);
-  f32x16 sacc = {};
+  f32x16 sacc = init;
 #pragma unroll
   for (int k = 0; k < NK; ++k) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], sacc, 0, 0, 0);
   // all LDS reads first, then the MFMA chain
@@ -749,24 +751,6 @@ __device__ __forceinline__ void tile_key_bias(float (&kb)[16], bool cen, int c, 
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (16 * ((i >> 2) & 1) + 8 * (i >> 3) + 4 * hh + (i & 3) == rt) kb[i] = bias_tail;
-  }
-}
-
-// The per-key terms of a centroid half tile in reweight mode: the bias of
-// each unselected block comes from the head's table cbt (log2 units) instead
-// of log2(n_c).  Four consecutive registers hold four consecutive keys.
-__device__ __forceinline__ void tile_key_bias_rw(float (&kb)[16], int c, int nb, uint32_t sbits, int hh,
-                                                 const float* cbt) {
-  const int nv = nb - 32 * c;
-  const uint32_t m = ((nv >= 32) ? 0u : ~((1u << max(nv, 0)) - 1u)) | sbits;
-  const uint32_t sb = m >> (4 * hh);
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int k0 = 16 * (g & 1) + 8 * (g >> 1);
-    const float4 t = *reinterpret_cast<const float4*>(cbt + 32 * c + k0 + 4 * hh);
-    const float tv[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) kb[4 * g + e] = ((sb >> (k0 + e)) & 1u) ? -INFINITY : tv[e];
   }
 }
 
@@ -821,7 +805,7 @@ __device__ __forceinline__ void tile_pv(const uint8_t* stage, int vblk, int lane
 }
 
 template <int D, int S, bool RW, bool Q8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attend_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Q8 ? 2 : 3, Q8 ? 2 : 3))) void attend_kernel(
     Shape s, const uint16_t* __restrict__ q, uint16_t* __restrict__ out, Workspace ws) {
   constexpr int NK = D / 16;          // QK k-steps = K blocks = PV MFMAs per tile
   constexpr int NDT = D / 32;         // 32-row d tiles of O^T
@@ -837,7 +821,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   __shared__ uint16_t ulist[SA_MAX_BLOCKS];  // union of the two lists
   __shared__ uint16_t uct[NW];               // centroid half tiles either needs
   __shared__ int info[8];
-  __shared__ __attribute__((aligned(16))) float cbs[RW ? SA_MAX_BLOCKS : 4];  // reweight centroid biases
+  __shared__ __attribute__((aligned(16))) float cbs[RW ? SA_MAX_BLOCKS : 4];  // reweight biases / c1
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -909,8 +893,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       info[4] = has1 ? 0 : 2 * nb;
     }
   } else {
-    if (RW)
-      for (int i = tid; i < s.nbp; i += 256) cbs[i] = ws.cbias[bh * s.nbp + i];
+    if (RW) {
+      const float inv_c1 = 1.0f / s.c1;
+      for (int i = tid; i < s.nbp; i += 256) cbs[i] = ws.cbias[bh * s.nbp + i] * inv_c1;
+    }
     const int cnt0 = min(max(ws.counts[bh * nb + a0], 0), nb);
     const int cnt1 = has1 ? min(max(ws.counts[bh * nb + a0 + 1], 0), nb) : 0;
     for (int i = tid; i < 2 * NW; i += 256) sel[i / NW][i % NW] = 0u;
@@ -999,7 +985,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const uint32_t my_dst =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring + w * PER * 1024;
   const uint8_t* const rd = ring;
-  const float bias_full = s.bias_full, bias_tail = s.bias_tail;
+  // (reweight mode: no log-mass term; its bias enters through the centroid
+  // tile's accumulator, see qk)
+  const float bias_full = RW ? 0.0f : s.bias_full, bias_tail = RW ? 0.0f : s.bias_tail;
 
   // Exact half tiles come first (the union is ascending) and only a ragged
   // last block and the centroid tiles need per-key terms, so the plain tiles
@@ -1042,22 +1030,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     return __builtin_amdgcn_readlane(tabv, v - tab_base);
   };
   // INT8 exact half tile: 1 KB blocks [codes 0 .. NT-1 | V^T 0 .. NK-1 |
-  // base record], block i copied by wave i % 4.
-  const uint8_t* k8_bh = ws.k8 + bh * nb * 64LL * D;
-  const uint16_t* vp_bh = ws.vp + bh * nb * 2LL * HT;
-  const uint16_t* kr_bh = ws.kbase + bh * nb * (long long)(D + 8);
+  // base record], block i copied by wave i % 4.  Per copy slot of this wave:
+  // the lane's source for key block 0 and the byte strides per half tile
+  // (codes, V^T) or per key block (the record, D/8 + 1 lanes).
+  constexpr int NQ = NT + NK + 1, PQ = (NQ + 3) / 4;
+  const uint8_t* qsrc[PQ];
+  int qht[PQ], qblk[PQ];
+  bool qlane[PQ];
+#pragma unroll
+  for (int i = 0; i < PQ; ++i) {
+    const int bi = w + 4 * i;
+    if (bi < NT) {
+      qsrc[i] = ws.k8 + bh * nb * 64LL * D + bi * 1024 + lane * 16;
+      qht[i] = 32 * D;
+      qblk[i] = 0;
+    } else if (bi < NT + NK) {
+      qsrc[i] = reinterpret_cast<const uint8_t*>(ws.vp + bh * nb * 2LL * HT + (bi - NT) * 512 + lane * 8);
+      qht[i] = 2 * HT;
+      qblk[i] = 0;
+    } else {
+      qsrc[i] = reinterpret_cast<const uint8_t*>(ws.kbase + bh * nb * (long long)(D + 8) + lane * 8);
+      qht[i] = 0;
+      qblk[i] = 2 * (D + 8);
+    }
+    qlane[i] = bi < NT + NK || (bi == NT + NK && lane <= D / 8);
+  }
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   auto copy_q8 = [&](int c, int ht, int stg) {
     const uint32_t base = ring_lds + stg * STAGE;
 #pragma unroll
-    for (int i = 0; i < (NT + NK + 4) / 4; ++i) {
-      const int bi = w + 4 * i;
-      if (bi < NT)
-        copy_one(k8_bh + (2LL * c + ht) * 32 * D + bi * 1024 + lane * 16, base + bi * 1024);
-      else if (bi < NT + NK)
-        copy_one(vp_bh + (2LL * c + ht) * HT + (bi - NT) * 512 + lane * 8, base + bi * 1024);
-      else if (bi == NT + NK && lane <= D / 8)
-        copy_one(kr_bh + (long long)c * (D + 8) + lane * 8, base + bi * 1024);
+    for (int i = 0; i < PQ; ++i) {
+      if (w + 4 * i < NQ && qlane[i])
+        copy_one(qsrc[i] + (long long)(2 * c + ht) * qht[i] + (long long)c * qblk[i], base + (w + 4 * i) * 1024);
     }
   };
   auto copy_tile = [&](int v, int e, int stg) {
@@ -1097,11 +1101,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   auto ring_next = [&]() { st = (st == S - 1) ? 0 : st + 1; };
   auto bias_of = [&](int u, int eu, float (&kb)[16]) {
     const bool cen = u >= TE;
-    if (RW && cen)
-      tile_key_bias_rw(kb, eu & 0xfff, nb, sel[x][eu & (NW - 1)], hh, cbs);
-    else
-      tile_key_bias(kb, cen, eu & 0xfff, u & 1, N, nb, sel[x][cen ? (eu & (NW - 1)) : 0], hh, bias_full,
-                    bias_tail);
+    tile_key_bias(kb, cen, eu & 0xfff, u & 1, N, nb, sel[x][cen ? (eu & (NW - 1)) : 0], hh, bias_full, bias_tail);
   };
 
   // Scores of a half tile.  The logit (log2 units) is sacc * ta + tb plus the
@@ -1110,22 +1110,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   // tile from the base record that follows V^T in the stage.
   float ta = c1, tb = 0.0f;
   int vblk = NK;  // first V^T block of the stage
-  auto qk = [&](int u, const uint8_t* stage) -> f32x16 {
+  auto qk_exact = [&](int u, const uint8_t* stage) -> f32x16 {  // u < TE
     if constexpr (Q8) {
-      if (u < TE) {
-        const uint8_t* rec = stage + (NT + NK) * 1024;
-        if (!(u & 1)) {
-          ta = c1 * (sq * *reinterpret_cast<const float*>(rec + 2 * D));
-          tb = c1 * mean_dot<NK>(rec, hh, qf);
-        }
-        vblk = NT;
-        return tile_qk_i8<NT>(stage, lane, q8);
+      const uint8_t* rec = stage + (NT + NK) * 1024;
+      if (!(u & 1)) {
+        ta = c1 * (sq * *reinterpret_cast<const float*>(rec + 2 * D));
+        tb = c1 * mean_dot<NK>(rec, hh, qf);
       }
+      vblk = NT;
+      return tile_qk_i8<NT>(stage, lane, q8);
+    }
+    return tile_qk<NK>(stage, lane, qf, f32x16{});
+  };
+  // Any half tile.  Reweight mode: the accumulator of a centroid tile starts
+  // at each block's bias / c1 (four consecutive registers hold four
+  // consecutive keys), so the logit carries the bias without a per-key term.
+  auto qk = [&](int u, int eu, const uint8_t* stage) -> f32x16 {
+    if constexpr (Q8) {
+      if (u < TE) return qk_exact(u, stage);
       ta = c1;
       tb = 0.0f;
       vblk = NK;
     }
-    return tile_qk<NK>(stage, lane, qf);
+    f32x16 init = {};
+    if constexpr (RW) {
+      if (u >= TE) {
+        const float* cb = cbs + 32 * (eu & 0xfff) + 4 * hh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 t = *reinterpret_cast<const float4*>(cb + 16 * (g & 1) + 8 * (g >> 1));
+          init[4 * g] = t.x;
+          init[4 * g + 1] = t.y;
+          init[4 * g + 2] = t.z;
+          init[4 * g + 3] = t.w;
+        }
+      }
+    }
+    return tile_qk<NK>(stage, lane, qf, init);
   };
   auto bias_t = [&](int u, int eu, float (&kb)[16]) {
     bias_of(u, eu, kb);
@@ -1145,7 +1166,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       for (int u = 0; u < TU; ++u) {
         const int eu = ring_step(u);
         if ((eu >> 12) & myflag) {
-          const f32x16 sacc = qk(u, rd + st * STAGE);
+          const f32x16 sacc = qk(u, eu, rd + st * STAGE);
           float kb[16];
           bias_t(u, eu, kb);
           mmax = fmaxf(mmax, tile_row_max(sacc, kb, ta));
@@ -1169,7 +1190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     if (u < TU) {
       const int eu = ring_step(u);
       const uint8_t* stage = rd + st * STAGE;
-      const f32x16 sacc = qk(u, stage);
+      const f32x16 sacc = qk(u, eu, stage);
       float kb[16];
       bias_t(u, eu, kb);
       if (!safe) {
@@ -1184,7 +1205,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       const int eu = ring_step(u);
       if ((eu >> 12) & myflag) {
         const uint8_t* stage = rd + st * STAGE;
-        const f32x16 sacc = qk(u, stage);
+        const f32x16 sacc = qk_exact(u, stage);
         float kb[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) kb[i] = 0.0f;
@@ -1196,7 +1217,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       const int eu = ring_step(u);
       if ((eu >> 12) & myflag) {
         const uint8_t* stage = rd + st * STAGE;
-        const f32x16 sacc = qk(u, stage);
+        const f32x16 sacc = qk(u, eu, stage);
         float kb[16];
         bias_t(u, eu, kb);
         tile_pv<NK, false>(stage, vblk, lane, sacc, kb, ta, 0.0f, mref, acc, lsum);
