@@ -53,6 +53,25 @@ What is computed, step by step, and where the pages state it:
    scale * (q . base_c + s_q * s_c * (q8 . r8)), q unquantised in the first
    term.  Codes are decided in float32, the precision the kernel uses;
    centroid logits are unchanged.
+7. Reblock (optional, reblock=True).  Spark-Reblock (Spark-H3 news,
+   Spark-Reblock bullet) replaces the fixed 64-row tiles by an input-, layer-
+   and head-dependent partition: two queries are alike when their score
+   patterns over the keys are alike, measured by the cosine in the metric of
+   the keys' second moment (and keys by that of the queries), and a
+   hierarchical partitioner splits groups until every leaf has the block
+   size, in O(N log N).  Reading: per (b, h) and side, M = Y^T Y over all N
+   rows of the other side, u_i = x_i / sqrt(x_i^T M x_i) for the rows after
+   the prefix blocks (prefix blocks stay in place), so that
+   cos_M(x_i, x_j) = u_i^T M u_j; a group of n > 64 rows with m = ceil(n/64)
+   blocks splits into a left child of 64 * ceil(m / 2) rows and the rest.
+   The pages do not give the split rule; it is taken as a pivot split that
+   uses only the stated similarity: a = the row least similar to the group's
+   mean direction (u_i^T M ubar), b = the row least similar to a, and the
+   left child is the rows ranked first by u_i^T M (u_b - u_a) (ties by
+   position), i.e. those most like a.  Children keep their parent's order,
+   left before right; the leaves in order are the new blocks.  Attention then
+   runs on Q, K, V permuted that way, and the output rows go back to their
+   positions.
 
 Readings where the pages leave a step open (each is argued in the design
 notes of this repository):
@@ -106,6 +125,9 @@ __all__ = [
     "forward",
     "reweight_summaries",
     "int8_qk_codes",
+    "mahalanobis_units",
+    "pivot_split",
+    "reblock_orders",
     "forward_blocks",
 ]
 
@@ -460,8 +482,93 @@ def _int8_head(d, b, h, rows):
     )
 
 
-def forward(q, k, v, **kw):
-    """Full output [B, N, H, D] float64 plus the routing info."""
+def mahalanobis_units(x, other):
+    """Rows u_i = x_i / ||x_i||_M of one head, M = other^T other (reading 7),
+    so that u_i^T M u_j is the cosine of the score patterns other @ x_i and
+    other @ x_j.  A row with ||x_i||_M = 0 maps to 0.  Returns (u, M)."""
+    x = np.asarray(x, dtype=np.float64)
+    other = np.asarray(other, dtype=np.float64)
+    M = other.T @ other
+    n2 = np.einsum("id,de,ie->i", x, M, x)
+    norm = np.sqrt(np.maximum(n2, 0.0))
+    u = np.where(norm[:, None] > 0, x / np.where(norm > 0, norm, 1.0)[:, None], 0.0)
+    return u, M
+
+
+def pivot_split(u, M, n_left):
+    """One split of a group (rows u [n, D] in group order), reading 7.
+    Returns (a, b, p, left): the two pivots (positions in the group, first
+    minimum on ties), the rank values p_i = u_i^T M (u_b - u_a) and the bool
+    mask of the n_left rows ranked first by (p_i, position)."""
+    u = np.asarray(u, dtype=np.float64)
+    n = u.shape[0]
+    s = u @ (M @ u.mean(axis=0))
+    a = int(np.argmin(s))
+    t = u @ (M @ u[a])
+    b = int(np.argmin(t))
+    p = u @ (M @ (u[b] - u[a]))
+    rank = np.lexsort((np.arange(n), p))
+    left = np.zeros(n, dtype=bool)
+    left[rank[:n_left]] = True
+    return a, b, p, left
+
+
+def _reblock_head(x, other, r0):
+    N = x.shape[0]
+    u, M = mahalanobis_units(x[r0:], other)
+
+    def rec(idx):
+        if len(idx) <= BLOCK:
+            return [idx]
+        m = -(-len(idx) // BLOCK)
+        n_left = BLOCK * (-(-m // 2))
+        left = pivot_split(u[idx], M, n_left)[3]
+        return rec(idx[left]) + rec(idx[~left])
+
+    leaves = rec(np.arange(N - r0)) if N > r0 else []
+    return np.concatenate([np.arange(r0)] + [r0 + leaf for leaf in leaves]).astype(np.int64)
+
+
+def reblock_orders(q, k, prefix_len: int = 0):
+    """Spark-Reblock orders (reading 7): perm_q, perm_k int64 [B, H, N];
+    new position i of a head holds original row perm[..., i].  Queries use
+    M = K^T K, keys (and with them values) M = Q^T Q."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, N, H, D = q.shape
+    r0 = min(prefix_blocks(prefix_len) * BLOCK, N)
+    pq = np.empty((B, H, N), dtype=np.int64)
+    pk = np.empty((B, H, N), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            pq[b, h] = _reblock_head(q[b, :, h], k[b, :, h], r0)
+            pk[b, h] = _reblock_head(k[b, :, h], q[b, :, h], r0)
+    return pq, pk
+
+
+def _gather_rows(x, perm):
+    x = np.asarray(x)
+    out = np.empty_like(x)
+    for b in range(x.shape[0]):
+        for h in range(x.shape[2]):
+            out[b, :, h] = x[b, perm[b, h], h]
+    return out
+
+
+def forward(q, k, v, reblock: bool = False, perms=None, **kw):
+    """Full output [B, N, H, D] float64 plus the routing info.  With
+    reblock=True the attention runs on the Spark-Reblock orders (``perms`` =
+    (perm_q, perm_k) to use given ones) and the rows are put back."""
+    if reblock:
+        pq, pk = perms if perms is not None else reblock_orders(q, k, kw.get("prefix_len", 0))
+        kw.pop("info", None)
+        out_p, info = forward(_gather_rows(q, pq), _gather_rows(k, pk), _gather_rows(v, pk), **kw)
+        out = np.empty_like(out_p)
+        for b in range(out.shape[0]):
+            for h in range(out.shape[2]):
+                out[b, pq[b, h], h] = out_p[b, :, h]
+        info["perm_q"], info["perm_k"] = pq, pk
+        return out, info
     B, N, H, D = q.shape
     nb = num_blocks(N)
     blocks = [(b, h, a) for b in range(B) for h in range(H) for a in range(nb)]

@@ -558,3 +558,85 @@ def test_int8_residual_beats_full_key_quantisation():
     print(f"relative L2: residual {rel(res):.4f}, whole keys {rel(full):.4f}")
     assert 0 < rel(res) < 0.03
     assert rel(res) < rel(full)
+
+
+# ------------------------------------------------------------- Spark-Reblock
+
+
+def test_reblock_metric_is_score_pattern_cosine():
+    """u_i^T M u_j with M = K^T K is the cosine of the score patterns K q_i
+    and K q_j, computed here directly over all keys."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((20, 16))
+    other = rng.standard_normal((300, 16))
+    u, M = O.mahalanobis_units(x, other)
+    S = x @ other.T  # score patterns
+    cos = (S @ S.T) / np.outer(np.linalg.norm(S, axis=1), np.linalg.norm(S, axis=1))
+    np.testing.assert_allclose(u @ M @ u.T, cos, rtol=0, atol=1e-12)
+
+
+def test_pivot_split_hand_example():
+    """Four unit rows with M = I, leaning towards (1, 0): the row least
+    similar to the mean direction is (0, 1); the row least similar to it is
+    (1, 0); ranking by u . ((1, 0) - (0, 1)) puts the two rows nearer (0, 1)
+    in the left child."""
+    c1, c3 = 1 / math.sqrt(0.82), 1 / math.sqrt(0.68)
+    u = np.array([[1.0, 0.0], [0.9 * c1, 0.1 * c1], [0.0, 1.0], [0.2 * c3, 0.8 * c3]])
+    a, b, p, left = O.pivot_split(u, np.eye(2), 2)
+    assert (a, b) == (2, 0)
+    np.testing.assert_allclose(p, [1.0, 0.8 * c1, -1.0, -0.6 * c3], atol=1e-12)
+    assert left.tolist() == [False, False, True, True]
+    # a metric that stretches the second axis changes the similarities
+    a2, b2, _, _ = O.pivot_split(u, np.diag([1.0, 9.0]), 2)
+    assert (a2, b2) != (a, b) or not np.allclose(O.pivot_split(u, np.diag([1.0, 9.0]), 2)[2], p)
+
+
+def test_reblock_recovers_planted_clusters():
+    """Queries drawn tightly around four directions (two blocks each) in
+    shuffled positions: every leaf of the partition holds one cluster only,
+    and the prefix rows stay in place."""
+    rng = np.random.default_rng(42)
+    B, N, H, D, pre = 1, 64 + 512, 1, 32, 64
+    centers = rng.standard_normal((4, D))
+    lab = np.repeat(np.arange(4), 128)
+    rng.shuffle(lab)
+    q = rng.standard_normal((B, N, H, D))
+    q[0, pre:, 0] = centers[lab] + 0.02 * rng.standard_normal((512, D))
+    k = rng.standard_normal((B, N, H, D))
+    pq, pk = O.reblock_orders(q, k, prefix_len=pre)
+    assert (pq[0, 0, :pre] == np.arange(pre)).all() and (pk[0, 0, :pre] == np.arange(pre)).all()
+    for perm in (pq, pk):
+        assert sorted(perm[0, 0].tolist()) == list(range(N))
+    blocks = (pq[0, 0, pre:] - pre).reshape(8, 64)
+    for blk in blocks:
+        assert len(set(lab[blk].tolist())) == 1
+
+
+def test_reblock_leaves_do_not_depend_on_row_order():
+    """Shuffling the rows after the prefix permutes the input but leaves the
+    partition (as sets of rows) unchanged: the split of a group depends only
+    on its set of rows (continuous data, no ties)."""
+    q, k, _ = _rand(1, 64 + 640, 2, 32, seed=43)
+    pre = 64
+    pq, pk = O.reblock_orders(q, k, prefix_len=pre)
+    rng = np.random.default_rng(44)
+    sh = np.concatenate([np.arange(pre), pre + rng.permutation(640)])
+    pq2, pk2 = O.reblock_orders(q[:, sh], k[:, sh], prefix_len=pre)
+    for p1, p2 in ((pq, pq2), (pk, pk2)):
+        for h in range(2):
+            a = {frozenset(bl) for bl in p1[0, h, pre:].reshape(10, 64).tolist()}
+            bset = {frozenset(sh[bl].tolist()) for bl in p2[0, h, pre:].reshape(10, 64)}
+            assert a == bset
+
+
+def test_reblock_keeps_dense_attention_and_changes_routed():
+    """Dense attention does not depend on the row order, so reblocking leaves
+    it unchanged; routed attention with centroids does change."""
+    q, k, v = _rand(1, 300, 2, 32, seed=45)
+    a, _ = O.forward(q, k, v, tau=-math.inf)
+    b, info = O.forward(q, k, v, tau=-math.inf, reblock=True, prefix_len=70)
+    np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+    assert not (info["perm_q"][0, 0] == np.arange(300)).all()
+    c, _ = O.forward(q, k, v, tau=1.0, prefix_len=70)
+    d, _ = O.forward(q, k, v, tau=1.0, prefix_len=70, reblock=True)
+    assert np.abs(c - d).max() > 1e-3
