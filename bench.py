@@ -129,7 +129,7 @@ def main():
     ap.add_argument("--workload", default="n32k", choices=["tiny", "n4k", "n16k", "n32k", "h3"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--no-modes", action="store_true", help="skip the reweight and INT8 QK^T timings")
+    ap.add_argument("--no-modes", action="store_true", help="skip the reweight, INT8 QK^T and reblock timings")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 256 MiB device copy before the steps (scales rocprofv3 byte counters)")
@@ -255,6 +255,24 @@ def main():
             print(f"# {name}: {m_call:.3f} ms/call (pool {m_pool:.3f}, attend {m_att:.3f})", file=sys.stderr,
                   flush=True)
             del mws, mplan
+        # Spark-Reblock runs through the forward call (partition + reorder +
+        # the path on the reordered copies + rows put back)
+        mplan = binding.SparseAttnPlan(B, N, H, D, prefix_len=w.prefix_len, reblock=True, **rkw)
+        mws = mplan.workspace(dev)
+        for _ in range(2):
+            mplan.forward(q, k, v, out=out, ws=mws)
+        torch.cuda.synchronize()
+        km = max(3, K // 2)
+        r0_ev, r1_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0_ev.record(stream)
+        for _ in range(km):
+            mplan.forward(q, k, v, out=out, ws=mws)
+        r1_ev.record(stream)
+        torch.cuda.synchronize()
+        m_call = r0_ev.elapsed_time(r1_ev) / km
+        modes["reblock"] = {"ms_per_call": round(m_call, 4)}
+        print(f"# reblock: {m_call:.3f} ms/call", file=sys.stderr, flush=True)
+        del mws, mplan
         torch.cuda.empty_cache()
 
     dense_flops = 4.0 * B * H * N * N * D

@@ -31,6 +31,7 @@ __all__ = [
     "SA_FLAG_EXACT_KV_ONLY",
     "SA_FLAG_REWEIGHT",
     "SA_FLAG_INT8_QK",
+    "SA_FLAG_REBLOCK",
 ]
 
 SA_ROUTE_TAU = 0
@@ -40,6 +41,7 @@ SA_FLAG_LOGMASS = 2
 SA_FLAG_EXACT_KV_ONLY = 4
 SA_FLAG_REWEIGHT = 8
 SA_FLAG_INT8_QK = 16
+SA_FLAG_REBLOCK = 32
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libsparse_attn.so"
@@ -88,12 +90,20 @@ class _Layout(ctypes.Structure):
         ("cbias", ctypes.c_uint64),
         ("k_int8", ctypes.c_uint64),
         ("kbase", ctypes.c_uint64),
+        ("rb_gram", ctypes.c_uint64),
+        ("rb_metric", ctypes.c_uint64),
+        ("rb_units", ctypes.c_uint64),
+        ("rb_order", ctypes.c_uint64),
+        ("rb_keys", ctypes.c_uint64),
+        ("rb_qkv", ctypes.c_uint64),
+        ("rb_out", ctypes.c_uint64),
         ("n_blocks", ctypes.c_int32),
         ("n_blocks_padded", ctypes.c_int32),
         ("tail_rows", ctypes.c_int32),
         ("prefix_blocks", ctypes.c_int32),
         ("topk", ctypes.c_int32),
         ("dense", ctypes.c_int32),
+        ("reblock_levels", ctypes.c_int32),
     ]
 
 
@@ -189,6 +199,7 @@ class SparseAttnPlan:
         logmass: bool = True,
         reweight: bool = False,
         int8_qk: bool = False,
+        reblock: bool = False,
         sm_scale: Optional[float] = None,
         in_strides: Optional[Tuple[int, int, int]] = None,
         out_strides: Optional[Tuple[int, int, int]] = None,
@@ -211,7 +222,7 @@ class SparseAttnPlan:
         p.sm_scale = float(sm_scale) if sm_scale else 0.0
         p.flags = ((SA_FLAG_CENTROID if centroid else 0) | (SA_FLAG_LOGMASS if logmass else 0)
                    | (SA_FLAG_EXACT_KV_ONLY if exact_kv_only else 0) | (SA_FLAG_REWEIGHT if reweight else 0)
-                   | (SA_FLAG_INT8_QK if int8_qk else 0))
+                   | (SA_FLAG_INT8_QK if int8_qk else 0) | (SA_FLAG_REBLOCK if reblock else 0))
         handle = ctypes.c_void_p()
         _check(lib.sparse_attn_plan_create(ctypes.byref(p), ctypes.byref(handle)), "sparse_attn_plan_create")
         self._lib = lib
@@ -349,6 +360,24 @@ class SparseAttnPlan:
         nbp = self.layout["n_blocks_padded"]
         return self._view(ws, "anchor", torch.float32, (B, H, D)), self._view(ws, "cbias", torch.float32, (B, H, nbp))
 
+    def reblock_views(self, ws):
+        """Spark-Reblock sections after ``forward`` with ``reblock=True``:
+        M fp32 [2, B, H, D, D] (side 0: K^T K for the query rows, side 1:
+        Q^T Q for the key rows), unit rows bf16 [2, B, H, n_v, D], and the
+        orders perm_q, perm_k int64 [B, H, N] (new position i holds input
+        row perm[..., i])."""
+        import torch
+
+        B, N, H, D = self.shape
+        r0 = min(self.layout["prefix_blocks"] * 64, N)
+        nv = N - r0
+        M = self._view(ws, "rb_metric", torch.float32, (2, B, H, D, D))
+        U = self._view(ws, "rb_units", torch.bfloat16, (2, B, H, nv, D))
+        ords = self._view(ws, "rb_order", torch.int32, (2, 2, B, H, nv))[self.layout["reblock_levels"] % 2]
+        head = torch.arange(r0, device=ws.device, dtype=torch.int64).expand(B, H, r0)
+        perms = [torch.cat([head, r0 + ords[side].to(torch.int64)], dim=2) for side in (0, 1)]
+        return M, U, perms[0], perms[1]
+
     def int8_views(self, ws):
         """INT8 QK^T sections written by the pool step with ``int8_qk=True``:
         residual codes int8 [B, H, n_b, 2, 32*D] (order in sparse_attn.h),
@@ -377,6 +406,7 @@ def sparse_attn(
     logmass: bool = True,
     reweight: bool = False,
     int8_qk: bool = False,
+    reblock: bool = False,
     sm_scale: Optional[float] = None,
     out=None,
     return_route: bool = False,
@@ -401,6 +431,7 @@ def sparse_attn(
         centroid=centroid,
         reweight=reweight,
         int8_qk=int8_qk,
+        reblock=reblock,
         logmass=logmass,
         sm_scale=sm_scale,
         in_strides=(q.stride(0), q.stride(1), q.stride(2)),

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libsparse_attn.so")
 
-SOURCES = ["sparse_attn_kernels.hip", "sparse_attn_api.cpp"]
+SOURCES = ["sparse_attn_kernels.hip", "reblock_kernels.hip", "sparse_attn_api.cpp"]
 
 # Packed fp32 instructions are switched off for all device code.
 HIP_FLAGS = [

@@ -8,6 +8,8 @@
 namespace sa {
 
 constexpr int kBlock = 64;
+constexpr int kGramChunk = 2048;  // rows per partial second moment (reblock)
+constexpr int kEmbedRows = 256;   // rows per embed workgroup (reblock)
 
 // Everything a launch needs, derived once by the plan.
 struct Shape {
@@ -31,6 +33,12 @@ struct Shape {
   float scale;              // softmax scale
   int prefix_len;
   int int8;                 // INT8 QK^T on the exact blocks
+  int reblock;              // Spark-Reblock orders (never on the dense path)
+  int rb_r0;                // first reordered row (prefix blocks stay)
+  int rb_n;                 // reordered rows per (b, h), N - rb_r0
+  int rb_levels;            // levels of the split tree
+  int rb_chunks;            // partial second moments per problem
+  int rb_P;                 // problems: 2 sides x B x H
 };
 
 // Device workspace sections (see the layout notes in sparse_attn.h).
@@ -48,6 +56,15 @@ struct Workspace {
   float* cbias;   // [B,H,nbp] reweight centroid bias, log2 units
   uint8_t* k8;     // [B,H,nb,2 half tiles] int8 residual codes, MFMA order
   uint16_t* kbase; // [B,H,nb] records: bf16 base row (D), fp32 scale, zero (D + 8 slots)
+  float* rb_part;  // [P, chunks, D, D] partial second moments
+  float* rb_M;     // [P, D, D] second moment of the other side
+  uint16_t* rb_U;  // [P, rb_n, D] bf16 unit rows in the metric
+  int* rb_ord;     // [2, P, rb_n] orders (ping-pong by level)
+  unsigned long long* rb_key;  // [P, rb_n] rank keys
+  uint16_t* rb_q;  // [B, N, H, D] reordered copies and output
+  uint16_t* rb_k;
+  uint16_t* rb_v;
+  uint16_t* rb_out;
 };
 
 hipError_t launch_pool_q(const Shape& s, const void* q, const Workspace& ws, hipStream_t stream);
@@ -55,6 +72,11 @@ hipError_t launch_anchor(const Shape& s, const void* q, const Workspace& ws, hip
 hipError_t launch_pack_kv(const Shape& s, const void* k, const void* v, const Workspace& ws,
                           hipStream_t stream);
 hipError_t launch_select(const Shape& s, const Workspace& ws, hipStream_t stream);
+hipError_t launch_reblock_partition(const Shape& s, const void* q, const void* k, const Workspace& ws,
+                                    hipStream_t stream);
+hipError_t launch_reblock_gather(const Shape& s, const void* q, const void* k, const void* v, const Workspace& ws,
+                                 hipStream_t stream);
+hipError_t launch_reblock_scatter(const Shape& s, void* out, const Workspace& ws, hipStream_t stream);
 hipError_t launch_attend(const Shape& s, const void* q, void* out, const Workspace& ws,
                          hipStream_t stream);
 

@@ -113,7 +113,8 @@ int validate_params(const sparse_attn_params& p) {
   if ((p.flags & SA_FLAG_REWEIGHT) && !(p.flags & SA_FLAG_CENTROID))
     return fail(SA_EINVAL, "SA_FLAG_REWEIGHT needs SA_FLAG_CENTROID");
   if (p.flags &
-      ~(SA_FLAG_CENTROID | SA_FLAG_LOGMASS | SA_FLAG_EXACT_KV_ONLY | SA_FLAG_REWEIGHT | SA_FLAG_INT8_QK))
+      ~(SA_FLAG_CENTROID | SA_FLAG_LOGMASS | SA_FLAG_EXACT_KV_ONLY | SA_FLAG_REWEIGHT | SA_FLAG_INT8_QK |
+        SA_FLAG_REBLOCK))
     return fail(SA_EINVAL, "unknown flag bits 0x%x", p.flags);
   return SA_OK;
 }
@@ -161,6 +162,15 @@ void build_plan(sparse_attn_plan* pl) {
   s.scale = (float)scale;
   s.prefix_len = p.prefix_len;
   s.int8 = (p.flags & SA_FLAG_INT8_QK) ? 1 : 0;
+  // Spark-Reblock: the rows after the prefix blocks are reordered; the split
+  // tree of n rows has ceil(log2(ceil(n / 64))) levels.
+  s.reblock = ((p.flags & SA_FLAG_REBLOCK) && !s.dense) ? 1 : 0;
+  s.rb_r0 = s.pb * sa::kBlock < p.N ? s.pb * sa::kBlock : p.N;
+  s.rb_n = p.N - s.rb_r0;
+  s.rb_levels = 0;
+  for (int m = (s.rb_n + sa::kBlock - 1) / sa::kBlock; (1 << s.rb_levels) < m;) ++s.rb_levels;
+  s.rb_chunks = (p.N + sa::kGramChunk - 1) / sa::kGramChunk;
+  s.rb_P = 2 * p.B * p.H;
 
   sparse_attn_ws_layout& L = pl->layout;
   std::memset(&L, 0, sizeof(L));
@@ -182,6 +192,15 @@ void build_plan(sparse_attn_plan* pl) {
   L.cbias = off; off = align256(off + bh * s.nbp * sizeof(float));
   L.k_int8 = off; off = align256(off + (s.int8 ? bh * s.nb * 64ull * p.D : 0));
   L.kbase = off; off = align256(off + (s.int8 ? bh * s.nb * (uint64_t)(p.D + 8) * sizeof(uint16_t) : 0));
+  const uint64_t rb = s.reblock ? 1 : 0;
+  const uint64_t P = 2 * bh, dd = (uint64_t)p.D * p.D, qkv = bh * (uint64_t)p.N * p.D * sizeof(uint16_t);
+  L.rb_gram = off; off = align256(off + rb * P * s.rb_chunks * dd * sizeof(float));
+  L.rb_metric = off; off = align256(off + rb * P * dd * sizeof(float));
+  L.rb_units = off; off = align256(off + rb * P * s.rb_n * (uint64_t)p.D * sizeof(uint16_t));
+  L.rb_order = off; off = align256(off + rb * 2 * P * s.rb_n * sizeof(int32_t));
+  L.rb_keys = off; off = align256(off + rb * P * s.rb_n * sizeof(uint64_t));
+  L.rb_qkv = off; off = align256(off + rb * 3 * qkv);
+  L.rb_out = off; off = align256(off + rb * qkv);
   L.total_bytes = off;
   L.n_blocks = s.nb;
   L.n_blocks_padded = s.nbp;
@@ -189,6 +208,7 @@ void build_plan(sparse_attn_plan* pl) {
   L.prefix_blocks = s.pb;
   L.topk = s.topk;
   L.dense = s.dense;
+  L.reblock_levels = s.reblock ? s.rb_levels : 0;
 }
 
 sa::Workspace carve(const sparse_attn_plan* pl, void* ws) {
@@ -208,6 +228,16 @@ sa::Workspace carve(const sparse_attn_plan* pl, void* ws) {
   w.cbias = reinterpret_cast<float*>(base + L.cbias);
   w.k8 = reinterpret_cast<uint8_t*>(base + L.k_int8);
   w.kbase = reinterpret_cast<uint16_t*>(base + L.kbase);
+  w.rb_part = reinterpret_cast<float*>(base + L.rb_gram);
+  w.rb_M = reinterpret_cast<float*>(base + L.rb_metric);
+  w.rb_U = reinterpret_cast<uint16_t*>(base + L.rb_units);
+  w.rb_ord = reinterpret_cast<int*>(base + L.rb_order);
+  w.rb_key = reinterpret_cast<unsigned long long*>(base + L.rb_keys);
+  const uint64_t qkv = (uint64_t)pl->params.B * pl->params.N * pl->params.H * pl->params.D;
+  w.rb_q = reinterpret_cast<uint16_t*>(base + L.rb_qkv);
+  w.rb_k = w.rb_q + qkv;
+  w.rb_v = w.rb_k + qkv;
+  w.rb_out = reinterpret_cast<uint16_t*>(base + L.rb_out);
   return w;
 }
 
@@ -279,6 +309,7 @@ int sparse_attn_workspace_layout(const sparse_attn_plan* plan, sparse_attn_ws_la
 int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
                      void* ws, size_t ws_bytes, void* stream) {
   if (!plan) return fail(SA_EINVAL, "plan is NULL");
+  if (plan->shape.reblock) return fail(SA_EINVAL, "SA_FLAG_REBLOCK runs through sparse_attn_forward only");
   int rc;
   if ((rc = check_tensors(q, k, v, nullptr, false))) return rc;
   if ((rc = check_ws(plan, ws, ws_bytes))) return rc;
@@ -295,6 +326,7 @@ int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k,
 
 int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, void* stream) {
   if (!plan) return fail(SA_EINVAL, "plan is NULL");
+  if (plan->shape.reblock) return fail(SA_EINVAL, "SA_FLAG_REBLOCK runs through sparse_attn_forward only");
   int rc;
   if ((rc = check_ws(plan, ws, ws_bytes))) return rc;
   if ((rc = check_device())) return rc;
@@ -306,6 +338,7 @@ int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, 
 int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, void* out, void* ws, size_t ws_bytes,
                        void* stream) {
   if (!plan) return fail(SA_EINVAL, "plan is NULL");
+  if (plan->shape.reblock) return fail(SA_EINVAL, "SA_FLAG_REBLOCK runs through sparse_attn_forward only");
   int rc;
   if ((rc = check_tensors(q, q, q, out, true))) return rc;
   if ((rc = check_ws(plan, ws, ws_bytes))) return rc;
@@ -324,17 +357,36 @@ int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void*
   if ((rc = check_device())) return rc;
   const sa::Workspace w = carve(plan, ws);
   hipStream_t st = (hipStream_t)stream;
-  if (!plan->shape.dense) {
-    if ((rc = launched(sa::launch_pool_q(plan->shape, q, w, st), "pool_q"))) return rc;
+  sa::Shape s = plan->shape;
+  void* o = out;
+  if (s.reblock) {
+    // partition, reorder Q, K, V into contiguous copies, run the path on
+    // them, and put the output rows back
+    if ((rc = launched(sa::launch_reblock_partition(s, q, k, w, st), "reblock partition"))) return rc;
+    if ((rc = launched(sa::launch_reblock_gather(s, q, k, v, w, st), "reblock gather"))) return rc;
+    const long long hd = (long long)s.H * s.D;
+    s.isb = s.osb = hd * s.N;
+    s.ist = s.ost = hd;
+    s.ish = s.osh = s.D;
+    q = w.rb_q;
+    k = w.rb_k;
+    v = w.rb_v;
+    o = w.rb_out;
   }
-  if (plan->shape.reweight) {
-    if ((rc = launched(sa::launch_anchor(plan->shape, q, w, st), "anchor"))) return rc;
+  if (!s.dense) {
+    if ((rc = launched(sa::launch_pool_q(s, q, w, st), "pool_q"))) return rc;
   }
-  if ((rc = launched(sa::launch_pack_kv(plan->shape, k, v, w, st), "pack_kv"))) return rc;
-  if (!plan->shape.dense) {
-    if ((rc = launched(sa::launch_select(plan->shape, w, st), "select"))) return rc;
+  if (s.reweight) {
+    if ((rc = launched(sa::launch_anchor(s, q, w, st), "anchor"))) return rc;
   }
-  if ((rc = launched(sa::launch_attend(plan->shape, q, out, w, st), "attend"))) return rc;
+  if ((rc = launched(sa::launch_pack_kv(s, k, v, w, st), "pack_kv"))) return rc;
+  if (!s.dense) {
+    if ((rc = launched(sa::launch_select(s, w, st), "select"))) return rc;
+  }
+  if ((rc = launched(sa::launch_attend(s, q, o, w, st), "attend"))) return rc;
+  if (s.reblock) {
+    if ((rc = launched(sa::launch_reblock_scatter(plan->shape, out, w, st), "reblock scatter"))) return rc;
+  }
   return ok();
 }
 

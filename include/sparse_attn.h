@@ -52,7 +52,7 @@ extern "C" {
 
 #define SA_BLOCK 64          /* rows per query / key block */
 #define SA_MAX_BLOCKS 2048   /* largest supported n_b = ceil(N / 64) */
-#define SA_ABI_VERSION 4
+#define SA_ABI_VERSION 5
 
 /* Routing modes (sparse_attn_params.route). */
 #define SA_ROUTE_TAU 0   /* S >= mean + tau * std; tau = -inf is the dense path */
@@ -86,6 +86,20 @@ extern "C" {
  * exact logit = scale * (q . base_c + s_q s_c (q8 . r8)).  Centroid logits
  * and P V are unchanged.  Without it (the default) QK^T is bf16. */
 #define SA_FLAG_INT8_QK 16u
+/* Spark-Reblock (comfyui-wiki "Spark-H3" news, Spark-Reblock bullet): an
+ * input-dependent block partition per (b, h).  Reading: queries are
+ * partitioned in the metric M = K^T K (the cosine of their score patterns
+ * over the keys), keys (with their values) in M = Q^T Q; rows after the
+ * prefix blocks only.  Unit rows u = x / sqrt(x^T M x); a group of n > 64
+ * rows splits into a left child of 64 ceil(ceil(n/64) / 2) rows and the
+ * rest: pivot a = the row least similar (u^T M ubar) to the group's mean
+ * direction, pivot b = the row least similar to a, and the left child takes
+ * the rows ranked first by u^T M (u_b - u_a), ties by position; children
+ * keep their parent's order.  The path then runs on Q, K, V in the new
+ * orders and the output rows are put back.  sparse_attn_forward only (the
+ * stage calls reject it); off on the dense path, whose result does not
+ * depend on the order. */
+#define SA_FLAG_REBLOCK 32u
 #define SA_FLAGS_DEFAULT (SA_FLAG_CENTROID | SA_FLAG_LOGMASS)
 
 /* Error codes. */
@@ -147,6 +161,19 @@ typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
  *   kbase             with SA_FLAG_INT8_QK only: per (b, h, block) a record
  *                     of D + 8 16-bit slots: the bf16 base row base_c, then
  *                     the fp32 block scale s_c in slots D, D + 1, then zero.
+ * With SA_FLAG_REBLOCK only (problem p = side * B * H + b * H + h, side 0 =
+ * query rows, side 1 = key rows; n_v = N - 64 * prefix_blocks rows move):
+ *   rb_gram           fp32 partial second moments (scratch).
+ *   rb_metric         fp32 [P, D, D]: M = Y^T Y of the other side.
+ *   rb_units          bf16 [P, n_v, D]: the unit rows u of the moving rows.
+ *   rb_order          int32 [2, P, n_v]: after sparse_attn_forward, buffer
+ *                     reblock_levels % 2 holds the final order: new
+ *                     position 64 * prefix_blocks + i holds row
+ *                     64 * prefix_blocks + order[p][i].
+ *   rb_keys           scratch; rb_qkv, rb_out: bf16 [B, N, H, D] copies of
+ *                     Q, K, V in the new orders and the output before the
+ *                     rows are put back (the sections above then describe
+ *                     these copies).
  * After sparse_attn_select:
  *   counts            int32 [B, H, n_b]: selected key blocks per query block.
  *   lists             int32 [B, H, n_b, n_b]: the selected key blocks in
@@ -160,12 +187,14 @@ typedef struct sparse_attn_ws_layout {
   uint64_t counts, lists;
   uint64_t anchor, cbias;
   uint64_t k_int8, kbase;
+  uint64_t rb_gram, rb_metric, rb_units, rb_order, rb_keys, rb_qkv, rb_out;
   int32_t n_blocks;        /* n_b */
   int32_t n_blocks_padded; /* n_bp */
   int32_t tail_rows;       /* valid rows of block n_b - 1 */
   int32_t prefix_blocks;   /* ceil(prefix_len / 64), capped at n_b */
   int32_t topk;            /* k of SA_ROUTE_TOPK, else 0 */
   int32_t dense;           /* 1 if tau = -inf: every block exact, no routing */
+  int32_t reblock_levels;  /* levels of the Spark-Reblock split tree, else 0 */
 } sparse_attn_ws_layout;
 
 /* Validates *params (host only, touches no device) and creates a plan.

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.sparse_attn_abi_version() == 4
+    assert lib.sparse_attn_abi_version() == 5
 
 
 def _params(**kw):
@@ -84,7 +84,7 @@ def _create(lib, p):
         (dict(prefix_len=1025), SA_EINVAL),
         (dict(prefix_len=1024), 0),
         (dict(sm_scale=float("inf")), SA_EINVAL),
-        (dict(flags=32), SA_EINVAL),
+        (dict(flags=64), SA_EINVAL),
         (dict(in_stride_b=3 * 1024 * 128, in_stride_t=3 * 128, in_stride_h=64), 0),
         (dict(in_stride_b=1024 * 128, in_stride_t=130, in_stride_h=64), SA_EALIGN),
         (dict(in_stride_b=0, in_stride_t=128, in_stride_h=64), SA_EINVAL),
@@ -116,14 +116,16 @@ def test_workspace_layout_matches_documented_sizes(int8_qk):
     assert L["n_blocks"] == nb and L["n_blocks_padded"] == 64
     assert L["tail_rows"] == 1000 - 64 * 15 and L["prefix_blocks"] == 2 and L["dense"] == 0
     names = ("qbar", "kbar", "vbar", "k_packed", "v_packed", "kbar_packed", "vbar_packed", "counts", "lists",
-             "anchor", "cbias", "k_int8", "kbase")
+             "anchor", "cbias", "k_int8", "kbase", "rb_gram", "rb_metric", "rb_units", "rb_order", "rb_keys",
+             "rb_qkv", "rb_out")
     offs = sorted((L[n], n) for n in names)
     sizes = dict(qbar=2 * 3 * nb * 128 * 4, kbar=2 * 3 * nb * 128 * 4, vbar=2 * 3 * nb * 128 * 4,
                  k_packed=2 * 3 * nb * 64 * 128 * 2, v_packed=2 * 3 * nb * 64 * 128 * 2,
                  kbar_packed=2 * 3 * 64 * 128 * 2, vbar_packed=2 * 3 * 64 * 128 * 2,
                  counts=2 * 3 * nb * 4, lists=2 * 3 * nb * nb * 4, anchor=2 * 3 * 128 * 4, cbias=2 * 3 * 64 * 4,
                  k_int8=2 * 3 * nb * 64 * 128 if int8_qk else 0,
-                 kbase=2 * 3 * nb * (128 + 8) * 2 if int8_qk else 0)
+                 kbase=2 * 3 * nb * (128 + 8) * 2 if int8_qk else 0,
+                 rb_gram=0, rb_metric=0, rb_units=0, rb_order=0, rb_keys=0, rb_qkv=0, rb_out=0)
     for (o, n), (o2, _) in zip(offs, offs[1:] + [(L["total_bytes"], "end")]):
         assert o % 256 == 0
         assert o2 - o >= sizes[n]
@@ -203,4 +205,32 @@ def test_int8_flag_is_accepted(lib):
     assert SA_FLAG_INT8_QK == 16
     for f in (3, 0, 3 | 8, 3 | 4):
         assert _create(lib, _params(flags=f | SA_FLAG_INT8_QK)) == 0
-    assert _create(lib, _params(flags=32)) == SA_EINVAL
+    assert _create(lib, _params(flags=64)) == SA_EINVAL
+
+
+def test_reblock_layout_and_stage_calls(lib):
+    """SA_FLAG_REBLOCK adds the partition sections (sizes as documented) and
+    runs through sparse_attn_forward only: the stage calls refuse the plan
+    before touching any device."""
+    from block_sparse_video_fp32_amd.binding import SA_FLAG_REBLOCK
+    assert SA_FLAG_REBLOCK == 32
+    B, N, H, D, pre = 2, 1000, 3, 128, 70
+    plan = binding.SparseAttnPlan(B, N, H, D, tau=1.0, prefix_len=pre, reblock=True)
+    L = plan.layout
+    nv, P = N - 128, 2 * B * H
+    assert L["reblock_levels"] == 4  # ceil(872 / 64) = 14 blocks
+    sizes = dict(rb_gram=P * 1 * D * D * 4, rb_metric=P * D * D * 4, rb_units=P * nv * D * 2,
+                 rb_order=2 * P * nv * 4, rb_keys=P * nv * 8, rb_qkv=3 * B * N * H * D * 2, rb_out=B * N * H * D * 2)
+    names = sorted(sizes, key=lambda n: L[n])
+    ends = [L[n] for n in names[1:]] + [L["total_bytes"]]
+    for n, e in zip(names, ends):
+        assert e - L[n] >= sizes[n], n
+    dense = binding.SparseAttnPlan(B, N, H, D, tau=-math.inf, reblock=True)
+    assert dense.layout["reblock_levels"] == 0  # no effect on the dense path
+    buf = ctypes.create_string_buffer(1 << 12)
+    addr = (ctypes.addressof(buf) + 255) // 256 * 256
+    for fn, args in ((lib.sparse_attn_pool, (addr, addr, addr, addr, 1 << 40, None)),
+                     (lib.sparse_attn_select, (addr, 1 << 40, None)),
+                     (lib.sparse_attn_attend, (addr, addr, addr, 1 << 40, None))):
+        assert fn(plan._h, *args) == SA_EINVAL
+        assert "sparse_attn_forward" in lib.sparse_attn_last_error().decode()

@@ -478,3 +478,183 @@ def test_workload_h3_sampled():
 
 def test_workload_n32k_int8_sampled():
     _sampled_parity("n32k", n_sample=24, int8_qk=True)
+
+
+# ------------------------------------------------------------- Spark-Reblock
+
+
+def _group_range(n, level, g):
+    """Node g at depth `level` of the split tree of n rows (as in the kernel)."""
+    start, size = 0, n
+    for t in range(level):
+        bit = (g >> (level - 1 - t)) & 1
+        if size <= 64:
+            if bit:
+                return start, 0
+            continue
+        m = -(-size // 64)
+        nl = 64 * (-(-m // 2))
+        if bit:
+            start, size = start + nl, size - nl
+        else:
+            size = nl
+    return start, size
+
+
+def _near_min(x, tol):
+    return np.nonzero(x <= x.min() + tol * max(1.0, np.abs(x).max()))[0]
+
+
+def check_reblock_splits(U, M, order, tol=1e-5):
+    """Every split of the GPU's tree, given its own unit rows U [n_v, D] and
+    metric M: the left child must be the n_L rows ranked first by the
+    oracle's pivot split of the same group, except rows within tol of the
+    cut; pivots within tol of the minimum are accepted as alternatives."""
+    nv = len(order)
+    levels = max(0, int(math.ceil(math.log2(max(1, -(-nv // 64))))))
+    n_split = 0
+    for level in range(levels):
+        for g in range(1 << level):
+            start, n = _group_range(nv, level, g)
+            if n <= 64:
+                continue
+            m = -(-n // 64)
+            nl = 64 * (-(-m // 2))
+            rows = order[start : start + n]
+            gpu_left = np.zeros(n, dtype=bool)
+            gpu_left[:nl] = True
+            u = U[rows]
+            a0, b0, p0, left0 = O.pivot_split(u, M, nl)
+            ok = False
+            s = u @ (M @ u.mean(axis=0))
+            for a in [a0] + [x for x in _near_min(s, tol) if x != a0]:
+                t = u @ (M @ u[a])
+                for b in ([b0] if a == a0 else []) + [x for x in _near_min(t, tol) if not (a == a0 and x == b0)]:
+                    p = u @ (M @ (u[b] - u[a]))
+                    ps = np.sort(p)
+                    thr = 0.5 * (ps[nl - 1] + ps[nl])
+                    d = tol * max(1.0, np.abs(p).max())
+                    if (p[gpu_left] <= thr + d).all() and (p[~gpu_left] >= thr - d).all():
+                        ok = True
+                        break
+                if ok:
+                    break
+            assert ok, f"level {level} group {g}: split differs from the oracle's ({(left0 != gpu_left).sum()} rows)"
+            n_split += 1
+    return n_split
+
+
+def _permute(x, perm):
+    out = np.empty_like(x)
+    for b in range(x.shape[0]):
+        for h in range(x.shape[2]):
+            out[b, :, h] = x[b, perm[b, h], h]
+    return out
+
+
+def reblock_parity(q, k, v, check_heads=None, **kw):
+    run = GpuRun(q, k, v, reblock=True, **kw)
+    M, U, pq, pk = run.plan.reblock_views(run.ws)
+    M = M.cpu().numpy().astype(np.float64)
+    pq, pk = pq.cpu().numpy(), pk.cpu().numpy()
+    B, N, H, D = q.shape
+    r0 = min(O.prefix_blocks(kw.get("prefix_len", 0)) * 64, N)
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    heads = [(b, h) for b in range(B) for h in range(H)] if check_heads is None else check_heads
+    n_split = 0
+    for side, (x, other, perm) in enumerate(((qf, kf, pq), (kf, qf, pk))):
+        for b in range(B):
+            for h in range(H):
+                assert sorted(perm[b, h].tolist()) == list(range(N))
+                assert (perm[b, h, :r0] == np.arange(r0)).all()
+        for b, h in heads:
+            u_ref, M_ref = O.mahalanobis_units(x[b, r0:, h], other[b, :, h])
+            np.testing.assert_allclose(M[side, b, h], M_ref, rtol=0, atol=1e-4 * np.abs(M_ref).max())
+            ug = U[side, b, h].float().cpu().numpy().astype(np.float64)
+            assert (np.abs(ug - u_ref) <= 2.0**-7 * np.abs(u_ref) + 2e-2 * np.abs(u_ref).max(axis=1, keepdims=True)).all()
+            n_split += check_reblock_splits(ug, M[side, b, h], perm[b, h, r0:] - r0)
+    print(f"  reblock: {n_split} splits validated", flush=True)
+    qp, kp, vp = _permute(qf, pq), _permute(kf, pk), _permute(vf, pk)
+    okw = oracle_kw(kw)
+    _, info = O.forward_blocks(qp, kp, vp, [], **okw)
+    sel = run.selection()
+    check_route(sel, info)
+    ref_p, _ = O.forward(qp, kp, vp, info=dict(info, sel=sel), **okw)
+    ref = np.empty_like(ref_p)
+    for b in range(B):
+        for h in range(H):
+            ref[b, pq[b, h], h] = ref_p[b, :, h]
+    check_output(run.out_f64(), ref, f"reblock N={N} {kw}")
+    return run, pq, pk
+
+
+REBLOCK = [
+    ("tau_prefix_d64", dict(B=1, N=1100, H=2, D=64), dict(tau=1.0, prefix_len=100)),
+    ("tau_d128", dict(B=1, N=1024, H=2, D=128), dict(tau=1.0)),
+    ("topk_tail_b2", dict(B=2, N=777, H=1, D=128), dict(topk_ratio=0.25, prefix_len=64)),
+    ("reweight_int8", dict(B=1, N=700, H=2, D=64), dict(tau=0.5, prefix_len=30, reweight=True, int8_qk=True)),
+    ("exact_kv", dict(B=1, N=1000, H=2, D=128), dict(tau=1.0, prefix_len=130, exact_kv_only=True)),
+    ("short", dict(B=1, N=100, H=2, D=64), dict(tau=1.0, prefix_len=40)),
+]
+
+
+@pytest.mark.parametrize("name,shape,kw", REBLOCK, ids=[r[0] for r in REBLOCK])
+def test_reblock_parity(name, shape, kw):
+    q, k, v = _small_inputs(shape, seed=len(name) + 100)
+    reblock_parity(q, k, v, **kw)
+
+
+def test_reblock_recovers_planted_clusters():
+    """Query rows tightly around four directions in shuffled positions: every
+    block of the GPU's query order holds one cluster."""
+    rng = np.random.default_rng(42)
+    B, N, H, D, pre = 1, 64 + 512, 1, 64, 64
+    centers = rng.standard_normal((4, D))
+    lab = np.repeat(np.arange(4), 128)
+    rng.shuffle(lab)
+    q = rng.standard_normal((B, N, H, D))
+    q[0, pre:, 0] = centers[lab] + 0.02 * rng.standard_normal((512, D))
+    k = rng.standard_normal((B, N, H, D))
+    v = rng.standard_normal((B, N, H, D))
+    bits = [inputs.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v)]
+    _, pq, _ = reblock_parity(*bits, tau=1.0, prefix_len=pre)
+    for blk in (pq[0, 0, pre:] - pre).reshape(8, 64):
+        assert len(set(lab[blk].tolist())) == 1
+
+
+def test_workload_n16k_reblock_sampled():
+    """n16k (H = 56) reordered: metric, unit rows and every split of four
+    heads per side, lists, and sampled output blocks."""
+    w = inputs.make_workload("n16k")
+    kw = dict(tau=w.tau, prefix_len=w.prefix_len)
+    run = GpuRun(w.q, w.k, w.v, reblock=True, **kw)
+    M, U, pq, pk = run.plan.reblock_views(run.ws)
+    M = M.cpu().numpy().astype(np.float64)
+    pq, pk = pq.cpu().numpy(), pk.cpu().numpy()
+    B, N, H, D = w.shape
+    r0 = min(O.prefix_blocks(w.prefix_len) * 64, N)
+    qf, kf, vf = _f32(w.q), _f32(w.k), _f32(w.v)
+    n_split = 0
+    for side, (x, other, perm) in enumerate(((qf, kf, pq), (kf, qf, pk))):
+        for h in (0, 17, 38, H - 1):
+            assert sorted(perm[0, h].tolist()) == list(range(N))
+            u_ref, M_ref = O.mahalanobis_units(x[0, r0:, h], other[0, :, h])
+            np.testing.assert_allclose(M[side, 0, h], M_ref, rtol=0, atol=1e-4 * np.abs(M_ref).max())
+            ug = U[side, 0, h].float().cpu().numpy().astype(np.float64)
+            n_split += check_reblock_splits(ug, M[side, 0, h], perm[0, h, r0:] - r0)
+    print(f"  n16k reblock: {n_split} splits validated", flush=True)
+    qp, kp, vp = _permute(qf, pq), _permute(kf, pk), _permute(vf, pk)
+    _, info = O.forward_blocks(qp, kp, vp, [], **kw)
+    sel = run.selection()
+    check_route(sel, info)
+    nb = O.num_blocks(N)
+    rng = np.random.default_rng(3)
+    blocks = sorted({(0, int(rng.integers(H)), int(rng.integers(nb))) for _ in range(24)} | {(0, 0, nb - 1)})
+    parts, _ = O.forward_blocks(qp, kp, vp, blocks, info=dict(info, sel=sel), **kw)
+    got = run.out_f64()
+    g, r = [], []
+    for (b, h, a), o in parts.items():
+        rows = pq[b, h, a * 64 : a * 64 + o.shape[0]]
+        g.append(got[b, rows, h])
+        r.append(o)
+    check_output(np.concatenate(g), np.concatenate(r), f"n16k reblock ({len(parts)} blocks)")
