@@ -270,8 +270,10 @@ def main():
         r1_ev.record(stream)
         torch.cuda.synchronize()
         m_call = r0_ev.elapsed_time(r1_ev) / km
-        modes["reblock"] = {"ms_per_call": round(m_call, 4)}
-        print(f"# reblock: {m_call:.3f} ms/call", file=sys.stderr, flush=True)
+        rb_flops, rb_density = selected_flops(mplan, mws, N, D)
+        modes["reblock"] = {"ms_per_call": round(m_call, 4), "density": round(rb_density, 5),
+                            "selected_tflop_per_call": round(rb_flops / 1e12, 4)}
+        print(f"# reblock: {m_call:.3f} ms/call, density {rb_density:.4f}", file=sys.stderr, flush=True)
         del mws, mplan
         torch.cuda.empty_cache()
 

@@ -93,6 +93,7 @@ class _Layout(ctypes.Structure):
         ("rb_gram", ctypes.c_uint64),
         ("rb_metric", ctypes.c_uint64),
         ("rb_units", ctypes.c_uint64),
+        ("rb_munits", ctypes.c_uint64),
         ("rb_order", ctypes.c_uint64),
         ("rb_keys", ctypes.c_uint64),
         ("rb_qkv", ctypes.c_uint64),
@@ -363,9 +364,9 @@ class SparseAttnPlan:
     def reblock_views(self, ws):
         """Spark-Reblock sections after ``forward`` with ``reblock=True``:
         M fp32 [2, B, H, D, D] (side 0: K^T K for the query rows, side 1:
-        Q^T Q for the key rows), unit rows bf16 [2, B, H, n_v, D], and the
-        orders perm_q, perm_k int64 [B, H, N] (new position i holds input
-        row perm[..., i])."""
+        Q^T Q for the key rows), unit rows u and M u bf16 [2, B, H, n_v, D],
+        and the orders perm_q, perm_k int64 [B, H, N] (new position i holds
+        input row perm[..., i])."""
         import torch
 
         B, N, H, D = self.shape
@@ -373,10 +374,11 @@ class SparseAttnPlan:
         nv = N - r0
         M = self._view(ws, "rb_metric", torch.float32, (2, B, H, D, D))
         U = self._view(ws, "rb_units", torch.bfloat16, (2, B, H, nv, D))
+        MU = self._view(ws, "rb_munits", torch.bfloat16, (2, B, H, nv, D))
         ords = self._view(ws, "rb_order", torch.int32, (2, 2, B, H, nv))[self.layout["reblock_levels"] % 2]
         head = torch.arange(r0, device=ws.device, dtype=torch.int64).expand(B, H, r0)
         perms = [torch.cat([head, r0 + ords[side].to(torch.int64)], dim=2) for side in (0, 1)]
-        return M, U, perms[0], perms[1]
+        return M, U, MU, perms[0], perms[1]
 
     def int8_views(self, ws):
         """INT8 QK^T sections written by the pool step with ``int8_qk=True``:

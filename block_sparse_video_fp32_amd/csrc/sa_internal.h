@@ -9,7 +9,7 @@ namespace sa {
 
 constexpr int kBlock = 64;
 constexpr int kGramChunk = 2048;  // rows per partial second moment (reblock)
-constexpr int kEmbedRows = 256;   // rows per embed workgroup (reblock)
+constexpr int kEmbedRows = 1024;  // rows per embed workgroup (reblock)
 
 // Everything a launch needs, derived once by the plan.
 struct Shape {
@@ -59,8 +59,9 @@ struct Workspace {
   float* rb_part;  // [P, chunks, D, D] partial second moments
   float* rb_M;     // [P, D, D] second moment of the other side
   uint16_t* rb_U;  // [P, rb_n, D] bf16 unit rows in the metric
+  uint16_t* rb_MU; // [P, rb_n, D] bf16 M u of the unit rows
   int* rb_ord;     // [2, P, rb_n] orders (ping-pong by level)
-  unsigned long long* rb_key;  // [P, rb_n] rank keys
+  uint32_t* rb_key;  // [P, rb_n] rank keys
   uint16_t* rb_q;  // [B, N, H, D] reordered copies and output
   uint16_t* rb_k;
   uint16_t* rb_v;

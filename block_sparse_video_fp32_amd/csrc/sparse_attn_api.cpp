@@ -197,8 +197,9 @@ void build_plan(sparse_attn_plan* pl) {
   L.rb_gram = off; off = align256(off + rb * P * s.rb_chunks * dd * sizeof(float));
   L.rb_metric = off; off = align256(off + rb * P * dd * sizeof(float));
   L.rb_units = off; off = align256(off + rb * P * s.rb_n * (uint64_t)p.D * sizeof(uint16_t));
+  L.rb_munits = off; off = align256(off + rb * P * s.rb_n * (uint64_t)p.D * sizeof(uint16_t));
   L.rb_order = off; off = align256(off + rb * 2 * P * s.rb_n * sizeof(int32_t));
-  L.rb_keys = off; off = align256(off + rb * P * s.rb_n * sizeof(uint64_t));
+  L.rb_keys = off; off = align256(off + rb * P * s.rb_n * sizeof(uint32_t));
   L.rb_qkv = off; off = align256(off + rb * 3 * qkv);
   L.rb_out = off; off = align256(off + rb * qkv);
   L.total_bytes = off;
@@ -231,8 +232,9 @@ sa::Workspace carve(const sparse_attn_plan* pl, void* ws) {
   w.rb_part = reinterpret_cast<float*>(base + L.rb_gram);
   w.rb_M = reinterpret_cast<float*>(base + L.rb_metric);
   w.rb_U = reinterpret_cast<uint16_t*>(base + L.rb_units);
+  w.rb_MU = reinterpret_cast<uint16_t*>(base + L.rb_munits);
   w.rb_ord = reinterpret_cast<int*>(base + L.rb_order);
-  w.rb_key = reinterpret_cast<unsigned long long*>(base + L.rb_keys);
+  w.rb_key = reinterpret_cast<uint32_t*>(base + L.rb_keys);
   const uint64_t qkv = (uint64_t)pl->params.B * pl->params.N * pl->params.H * pl->params.D;
   w.rb_q = reinterpret_cast<uint16_t*>(base + L.rb_qkv);
   w.rb_k = w.rb_q + qkv;

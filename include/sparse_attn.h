@@ -166,6 +166,8 @@ typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
  *   rb_gram           fp32 partial second moments (scratch).
  *   rb_metric         fp32 [P, D, D]: M = Y^T Y of the other side.
  *   rb_units          bf16 [P, n_v, D]: the unit rows u of the moving rows.
+ *   rb_munits         bf16 [P, n_v, D]: M u of the same rows (the split
+ *                     compares rows through these).
  *   rb_order          int32 [2, P, n_v]: after sparse_attn_forward, buffer
  *                     reblock_levels % 2 holds the final order: new
  *                     position 64 * prefix_blocks + i holds row
@@ -187,7 +189,7 @@ typedef struct sparse_attn_ws_layout {
   uint64_t counts, lists;
   uint64_t anchor, cbias;
   uint64_t k_int8, kbase;
-  uint64_t rb_gram, rb_metric, rb_units, rb_order, rb_keys, rb_qkv, rb_out;
+  uint64_t rb_gram, rb_metric, rb_units, rb_munits, rb_order, rb_keys, rb_qkv, rb_out;
   int32_t n_blocks;        /* n_b */
   int32_t n_blocks_padded; /* n_bp */
   int32_t tail_rows;       /* valid rows of block n_b - 1 */

@@ -495,18 +495,20 @@ def mahalanobis_units(x, other):
     return u, M
 
 
-def pivot_split(u, M, n_left):
+def pivot_split(u, M, n_left, mu=None):
     """One split of a group (rows u [n, D] in group order), reading 7.
     Returns (a, b, p, left): the two pivots (positions in the group, first
     minimum on ties), the rank values p_i = u_i^T M (u_b - u_a) and the bool
-    mask of the n_left rows ranked first by (p_i, position)."""
+    mask of the n_left rows ranked first by (p_i, position).  ``mu`` may
+    give the rows M u_i (M is symmetric, so u_i^T M v = (M u_i) . v)."""
     u = np.asarray(u, dtype=np.float64)
     n = u.shape[0]
-    s = u @ (M @ u.mean(axis=0))
+    mu = u @ M if mu is None else np.asarray(mu, dtype=np.float64)
+    s = mu @ u.mean(axis=0)
     a = int(np.argmin(s))
-    t = u @ (M @ u[a])
+    t = mu @ u[a]
     b = int(np.argmin(t))
-    p = u @ (M @ (u[b] - u[a]))
+    p = mu @ (u[b] - u[a])
     rank = np.lexsort((np.arange(n), p))
     left = np.zeros(n, dtype=bool)
     left[rank[:n_left]] = True

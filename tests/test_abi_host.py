@@ -116,8 +116,8 @@ def test_workspace_layout_matches_documented_sizes(int8_qk):
     assert L["n_blocks"] == nb and L["n_blocks_padded"] == 64
     assert L["tail_rows"] == 1000 - 64 * 15 and L["prefix_blocks"] == 2 and L["dense"] == 0
     names = ("qbar", "kbar", "vbar", "k_packed", "v_packed", "kbar_packed", "vbar_packed", "counts", "lists",
-             "anchor", "cbias", "k_int8", "kbase", "rb_gram", "rb_metric", "rb_units", "rb_order", "rb_keys",
-             "rb_qkv", "rb_out")
+             "anchor", "cbias", "k_int8", "kbase", "rb_gram", "rb_metric", "rb_units", "rb_munits", "rb_order",
+             "rb_keys", "rb_qkv", "rb_out")
     offs = sorted((L[n], n) for n in names)
     sizes = dict(qbar=2 * 3 * nb * 128 * 4, kbar=2 * 3 * nb * 128 * 4, vbar=2 * 3 * nb * 128 * 4,
                  k_packed=2 * 3 * nb * 64 * 128 * 2, v_packed=2 * 3 * nb * 64 * 128 * 2,
@@ -125,7 +125,7 @@ def test_workspace_layout_matches_documented_sizes(int8_qk):
                  counts=2 * 3 * nb * 4, lists=2 * 3 * nb * nb * 4, anchor=2 * 3 * 128 * 4, cbias=2 * 3 * 64 * 4,
                  k_int8=2 * 3 * nb * 64 * 128 if int8_qk else 0,
                  kbase=2 * 3 * nb * (128 + 8) * 2 if int8_qk else 0,
-                 rb_gram=0, rb_metric=0, rb_units=0, rb_order=0, rb_keys=0, rb_qkv=0, rb_out=0)
+                 rb_gram=0, rb_metric=0, rb_units=0, rb_munits=0, rb_order=0, rb_keys=0, rb_qkv=0, rb_out=0)
     for (o, n), (o2, _) in zip(offs, offs[1:] + [(L["total_bytes"], "end")]):
         assert o % 256 == 0
         assert o2 - o >= sizes[n]
@@ -220,7 +220,7 @@ def test_reblock_layout_and_stage_calls(lib):
     nv, P = N - 128, 2 * B * H
     assert L["reblock_levels"] == 4  # ceil(872 / 64) = 14 blocks
     sizes = dict(rb_gram=P * 1 * D * D * 4, rb_metric=P * D * D * 4, rb_units=P * nv * D * 2,
-                 rb_order=2 * P * nv * 4, rb_keys=P * nv * 8, rb_qkv=3 * B * N * H * D * 2, rb_out=B * N * H * D * 2)
+                 rb_munits=P * nv * D * 2, rb_order=2 * P * nv * 4, rb_keys=P * nv * 4, rb_qkv=3 * B * N * H * D * 2, rb_out=B * N * H * D * 2)
     names = sorted(sizes, key=lambda n: L[n])
     ends = [L[n] for n in names[1:]] + [L["total_bytes"]]
     for n, e in zip(names, ends):

@@ -505,11 +505,12 @@ def _near_min(x, tol):
     return np.nonzero(x <= x.min() + tol * max(1.0, np.abs(x).max()))[0]
 
 
-def check_reblock_splits(U, M, order, tol=1e-5):
-    """Every split of the GPU's tree, given its own unit rows U [n_v, D] and
-    metric M: the left child must be the n_L rows ranked first by the
-    oracle's pivot split of the same group, except rows within tol of the
-    cut; pivots within tol of the minimum are accepted as alternatives."""
+def check_reblock_splits(U, M, order, MU=None, tol=1e-5):
+    """Every split of the GPU's tree, given its own unit rows U [n_v, D], the
+    rows M u (MU, the GPU's, when given) and metric M: the left child must be
+    the n_L rows ranked first by the oracle's pivot split of the same group,
+    except rows within tol of the cut; pivots within tol of the minimum are
+    accepted as alternatives."""
     nv = len(order)
     levels = max(0, int(math.ceil(math.log2(max(1, -(-nv // 64))))))
     n_split = 0
@@ -524,13 +525,14 @@ def check_reblock_splits(U, M, order, tol=1e-5):
             gpu_left = np.zeros(n, dtype=bool)
             gpu_left[:nl] = True
             u = U[rows]
-            a0, b0, p0, left0 = O.pivot_split(u, M, nl)
+            mu = u @ M if MU is None else MU[rows]
+            a0, b0, p0, left0 = O.pivot_split(u, M, nl, mu=mu)
             ok = False
-            s = u @ (M @ u.mean(axis=0))
+            s = mu @ u.mean(axis=0)
             for a in [a0] + [x for x in _near_min(s, tol) if x != a0]:
-                t = u @ (M @ u[a])
+                t = mu @ u[a]
                 for b in ([b0] if a == a0 else []) + [x for x in _near_min(t, tol) if not (a == a0 and x == b0)]:
-                    p = u @ (M @ (u[b] - u[a]))
+                    p = mu @ (u[b] - u[a])
                     ps = np.sort(p)
                     thr = 0.5 * (ps[nl - 1] + ps[nl])
                     d = tol * max(1.0, np.abs(p).max())
@@ -554,7 +556,7 @@ def _permute(x, perm):
 
 def reblock_parity(q, k, v, check_heads=None, **kw):
     run = GpuRun(q, k, v, reblock=True, **kw)
-    M, U, pq, pk = run.plan.reblock_views(run.ws)
+    M, U, MU, pq, pk = run.plan.reblock_views(run.ws)
     M = M.cpu().numpy().astype(np.float64)
     pq, pk = pq.cpu().numpy(), pk.cpu().numpy()
     B, N, H, D = q.shape
@@ -572,7 +574,10 @@ def reblock_parity(q, k, v, check_heads=None, **kw):
             np.testing.assert_allclose(M[side, b, h], M_ref, rtol=0, atol=1e-4 * np.abs(M_ref).max())
             ug = U[side, b, h].float().cpu().numpy().astype(np.float64)
             assert (np.abs(ug - u_ref) <= 2.0**-7 * np.abs(u_ref) + 2e-2 * np.abs(u_ref).max(axis=1, keepdims=True)).all()
-            n_split += check_reblock_splits(ug, M[side, b, h], perm[b, h, r0:] - r0)
+            mug = MU[side, b, h].float().cpu().numpy().astype(np.float64)
+            mref = ug @ M[side, b, h]
+            assert (np.abs(mug - mref) <= 2.0**-6 * np.abs(mref) + 2e-2 * np.abs(mref).max(axis=1, keepdims=True)).all()
+            n_split += check_reblock_splits(ug, M[side, b, h], perm[b, h, r0:] - r0, MU=mug)
     print(f"  reblock: {n_split} splits validated", flush=True)
     qp, kp, vp = _permute(qf, pq), _permute(kf, pk), _permute(vf, pk)
     okw = oracle_kw(kw)
@@ -628,7 +633,7 @@ def test_workload_n16k_reblock_sampled():
     w = inputs.make_workload("n16k")
     kw = dict(tau=w.tau, prefix_len=w.prefix_len)
     run = GpuRun(w.q, w.k, w.v, reblock=True, **kw)
-    M, U, pq, pk = run.plan.reblock_views(run.ws)
+    M, U, MU, pq, pk = run.plan.reblock_views(run.ws)
     M = M.cpu().numpy().astype(np.float64)
     pq, pk = pq.cpu().numpy(), pk.cpu().numpy()
     B, N, H, D = w.shape
@@ -641,7 +646,8 @@ def test_workload_n16k_reblock_sampled():
             u_ref, M_ref = O.mahalanobis_units(x[0, r0:, h], other[0, :, h])
             np.testing.assert_allclose(M[side, 0, h], M_ref, rtol=0, atol=1e-4 * np.abs(M_ref).max())
             ug = U[side, 0, h].float().cpu().numpy().astype(np.float64)
-            n_split += check_reblock_splits(ug, M[side, 0, h], perm[0, h, r0:] - r0)
+            mug = MU[side, 0, h].float().cpu().numpy().astype(np.float64)
+            n_split += check_reblock_splits(ug, M[side, 0, h], perm[0, h, r0:] - r0, MU=mug)
     print(f"  n16k reblock: {n_split} splits validated", flush=True)
     qp, kp, vp = _permute(qf, pq), _permute(kf, pk), _permute(vf, pk)
     _, info = O.forward_blocks(qp, kp, vp, [], **kw)
