@@ -317,7 +317,7 @@ def main():
         "pool_gbs": round(pool_bytes / (t_pool * 1e-3) / 1e9, 1),
         "select_gbs": round(sel_bytes / (t_sel * 1e-3) / 1e9, 1),
         "roofline": {
-            "kernel": "attend_kernel<128, 2, false>",
+            "kernel": "attend_kernel<128, 2, false, false>",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
