@@ -664,3 +664,36 @@ def test_workload_n16k_reblock_sampled():
         g.append(got[b, rows, h])
         r.append(o)
     check_output(np.concatenate(g), np.concatenate(r), f"n16k reblock ({len(parts)} blocks)")
+
+
+def test_reblock_strided_views_and_reruns():
+    """Reblock on strided views of a fused [B, N, 3, H, D] projection, writing
+    into a strided output, matches reblock on contiguous inputs bit for bit,
+    and a rerun on the same workspace repeats orders and output exactly."""
+    dev = _dev()
+    B, N, H, D = 2, 1300, 3, 128
+    q, k, v = inputs.clustered(B, N, H, D, seed=19)
+    fused = np.stack([q, k, v], axis=2)
+    ft = inputs.to_torch_bf16(fused, dev)
+    tq, tk, tv = ft[:, :, 0], ft[:, :, 1], ft[:, :, 2]
+    out_big = torch.zeros((B, N, 2, H, D), dtype=torch.bfloat16, device=dev)
+    out = out_big[:, :, 1]
+    binding.sparse_attn(tq, tk, tv, tau=1.0, prefix_len=90, reblock=True, out=out)
+    torch.cuda.synchronize()
+    ref = GpuRun(q, k, v, tau=1.0, prefix_len=90, reblock=True)
+    assert torch.equal(out.contiguous().view(torch.int16), ref.out.view(torch.int16))
+    assert (out_big[:, :, 0] == 0).all()
+    _, _, _, pq1, pk1 = ref.plan.reblock_views(ref.ws)
+    pq1, pk1, o1 = pq1.clone(), pk1.clone(), ref.out.clone()
+    ref.plan.forward(ref.q, ref.k, ref.v, out=ref.out, ws=ref.ws)
+    torch.cuda.synchronize()
+    _, _, _, pq2, pk2 = ref.plan.reblock_views(ref.ws)
+    assert torch.equal(pq1, pq2) and torch.equal(pk1, pk2)
+    assert torch.equal(o1.view(torch.int16), ref.out.view(torch.int16))
+
+
+def test_reblock_d64_deeper_tree():
+    """D = 64, 4160 moving rows (66 blocks, a 7-level tree with ragged
+    groups): every split of every head against the oracle."""
+    q, k, v = inputs.clustered(1, 4224, 2, 64, seed=23)
+    reblock_parity(q, k, v, tau=1.0, prefix_len=64)
