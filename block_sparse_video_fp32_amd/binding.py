@@ -143,6 +143,10 @@ def load_library() -> ctypes.CDLL:
         lib.sparse_attn_pool.restype = i32
         lib.sparse_attn_select.argtypes = [vp, vp, sz, vp]
         lib.sparse_attn_select.restype = i32
+        lib.sparse_attn_route.argtypes = [vp, vp, vp, vp, vp, sz, vp]
+        lib.sparse_attn_route.restype = i32
+        lib.sparse_attn_workspace_bytes.argtypes = [vp, ctypes.POINTER(sz)]
+        lib.sparse_attn_workspace_bytes.restype = i32
         lib.sparse_attn_attend.argtypes = [vp, vp, vp, vp, sz, vp]
         lib.sparse_attn_attend.restype = i32
         lib.sparse_attn_strerror.argtypes = [i32]
@@ -243,7 +247,9 @@ class SparseAttnPlan:
 
     @property
     def workspace_bytes(self) -> int:
-        return int(self.layout["total_bytes"])
+        n = ctypes.c_size_t()
+        _check(self._lib.sparse_attn_workspace_bytes(self._h, ctypes.byref(n)), "sparse_attn_workspace_bytes")
+        return int(n.value)
 
     @property
     def dense(self) -> bool:
@@ -297,6 +303,14 @@ class SparseAttnPlan:
         self._check_io(q, k, v)
         ws = self.workspace(q.device) if ws is None else ws
         self._call(self._lib.sparse_attn_pool, "sparse_attn_pool", q.device,
+                   _ptr(q), _ptr(k), _ptr(v), _ptr(ws), ws.numel())
+        return ws
+
+    def route(self, q, k, v, ws=None):
+        """Steps 1-3 (pool and select): counts and lists in ws."""
+        self._check_io(q, k, v)
+        ws = self.workspace(q.device) if ws is None else ws
+        self._call(self._lib.sparse_attn_route, "sparse_attn_route", q.device,
                    _ptr(q), _ptr(k), _ptr(v), _ptr(ws), ws.numel())
         return ws
 

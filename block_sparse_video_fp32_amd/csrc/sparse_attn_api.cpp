@@ -326,6 +326,19 @@ int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k,
   return ok();
 }
 
+int sparse_attn_workspace_bytes(const sparse_attn_plan* plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(SA_EINVAL, "plan and bytes must be non-NULL");
+  *bytes = (size_t)plan->layout.total_bytes;
+  return ok();
+}
+
+int sparse_attn_route(const sparse_attn_plan* plan, const void* q, const void* k, const void* v, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc = sparse_attn_pool(plan, q, k, v, ws, ws_bytes, stream);
+  if (rc || plan->shape.dense) return rc;
+  return sparse_attn_select(plan, ws, ws_bytes, stream);
+}
+
 int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, void* stream) {
   if (!plan) return fail(SA_EINVAL, "plan is NULL");
   if (plan->shape.reblock) return fail(SA_EINVAL, "SA_FLAG_REBLOCK runs through sparse_attn_forward only");

@@ -210,6 +210,10 @@ void sparse_attn_plan_destroy(sparse_attn_plan* plan);
 /* Fills *layout for the plan's shape (host only). */
 int sparse_attn_workspace_layout(const sparse_attn_plan* plan, sparse_attn_ws_layout* layout);
 
+/* *bytes = the device workspace a call with this plan needs
+ * (layout.total_bytes; host only). */
+int sparse_attn_workspace_bytes(const sparse_attn_plan* plan, size_t* bytes);
+
 /* Full forward: pool, select and attend (pool and attend alone on the dense
  * path) enqueued on `stream` (a hipStream_t; NULL is the null stream).
  * q, k, v are read-only bf16 device pointers and may alias one another; out
@@ -228,6 +232,13 @@ int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k,
  * in ws and writes counts and lists (threshold or top-K, sink, dense
  * prefix rows). */
 int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, void* stream);
+
+/* Steps 1-3: the routing of every query block (sparse_attn_pool followed
+ * by sparse_attn_select), leaving counts and lists in ws for inspection or
+ * for sparse_attn_attend.  Same arguments and errors as sparse_attn_pool;
+ * on the dense path it only pools (there is nothing to route). */
+int sparse_attn_route(const sparse_attn_plan* plan, const void* q, const void* k, const void* v, void* ws,
+                      size_t ws_bytes, void* stream);
 
 /* Step 4 alone: exact attention over each query block's list and centroid
  * terms for every other block, reading q and, from ws, the packed tiles,

@@ -234,3 +234,13 @@ def test_reblock_layout_and_stage_calls(lib):
                      (lib.sparse_attn_attend, (addr, addr, addr, 1 << 40, None))):
         assert fn(plan._h, *args) == SA_EINVAL
         assert "sparse_attn_forward" in lib.sparse_attn_last_error().decode()
+
+
+def test_workspace_bytes_and_route_entry_points(lib):
+    """sparse_attn_workspace_bytes reports the layout's total; the route
+    call validates like the pool call (refused before any launch)."""
+    plan = binding.SparseAttnPlan(1, 1000, 2, 64, tau=1.0)
+    assert plan.workspace_bytes == plan.layout["total_bytes"] > 0
+    n = ctypes.c_size_t()
+    assert lib.sparse_attn_workspace_bytes(None, ctypes.byref(n)) == SA_EINVAL
+    assert lib.sparse_attn_route(plan._h, None, None, None, None, 0, None) == SA_EINVAL

@@ -697,3 +697,23 @@ def test_reblock_d64_deeper_tree():
     groups): every split of every head against the oracle."""
     q, k, v = inputs.clustered(1, 4224, 2, 64, seed=23)
     reblock_parity(q, k, v, tau=1.0, prefix_len=64)
+
+
+def test_route_entry_point_matches_stages():
+    """sparse_attn_route leaves the same counts and lists as pool + select."""
+    dev = _dev()
+    q, k, v = inputs.clustered(1, 1500, 2, 128, seed=31)
+    tq, tk, tv = (inputs.to_torch_bf16(x, dev) for x in (q, k, v))
+    plan = binding.SparseAttnPlan(1, 1500, 2, 128, topk_ratio=0.2, prefix_len=70)
+    ws1 = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    ws2 = torch.empty_like(ws1)
+    plan.route(tq, tk, tv, ws1)
+    plan.pool(tq, tk, tv, ws2)
+    plan.select(ws2)
+    torch.cuda.synchronize()
+    c1, l1 = plan.route_views(ws1)
+    c2, l2 = plan.route_views(ws2)
+    assert torch.equal(c1, c2)
+    nb = c1.shape[-1]
+    valid = torch.arange(nb, device=dev).view(1, 1, 1, nb) < c1.unsqueeze(-1)
+    assert torch.equal(torch.where(valid, l1, 0), torch.where(valid, l2, 0))
