@@ -401,7 +401,8 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
 }
 
 // ---------------------------------------------------------------------------
-// select: grid (ceil(n_b / 16), H, B), 256 threads, dynamic LDS.
+// select: grid ceil(n_b / 16) * H * B (XCD-grouped by head), 256 threads,
+// dynamic LDS.
 // Phase 1: S[r][c] = Qbar_(a0+r) . Kbar_c for 16 query blocks and every key
 // block, an fp32 GEMM on v_mfma_f32_16x16x4_f32.  Phase 2: wave w routes rows
 // 4w .. 4w + 3.
@@ -422,8 +423,15 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
   int* hist = reinterpret_cast<int*>(S + R * s.nb);  // [4][256]
 
   const int nb = s.nb;
-  const int a0 = blockIdx.x * R;
-  const int h = blockIdx.y, b = blockIdx.z;
+  // One-dimensional grid, remapped so that the workgroups of one head run on
+  // one XCD (workgroups go to the 8 XCDs round-robin), which then fetches
+  // that head's Kbar into its L2 once.
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, kx = bid >> 3, qq = G >> 3, rr = G & 7;
+  const int lid = (xcd < rr) ? xcd * (qq + 1) + kx : rr * (qq + 1) + (xcd - rr) * qq + kx;
+  const int ngroups = (s.nb + R - 1) / R;
+  const int a0 = (lid % ngroups) * R;
+  const int h = (lid / ngroups) % s.H, b = lid / (ngroups * s.H);
   const long long bh = (long long)b * s.H + h;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
@@ -1284,7 +1292,7 @@ hipError_t launch_select_t(const Shape& s, const Workspace& ws, hipStream_t stre
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<D>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  dim3 grid((s.nb + 15) / 16, s.H, s.B);
+  dim3 grid((unsigned)(((s.nb + 15) / 16) * s.H * s.B));
   hipLaunchKernelGGL((select_kernel<D>), grid, dim3(256), lds, stream, s, ws);
   return hipGetLastError();
 }
