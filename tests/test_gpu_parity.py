@@ -717,3 +717,25 @@ def test_route_entry_point_matches_stages():
     nb = c1.shape[-1]
     valid = torch.arange(nb, device=dev).view(1, 1, 1, nb) < c1.unsqueeze(-1)
     assert torch.equal(torch.where(valid, l1, 0), torch.where(valid, l2, 0))
+
+
+# ------------------------------------------------------- mode combinations
+
+_COMBOS = []
+for _i, (_D, _B, _N, _pre) in enumerate([(64, 2, 333, 0), (128, 1, 700, 70), (64, 1, 1000, 1000), (128, 2, 450, 130)]):
+    for _flags in ({}, dict(reweight=True), dict(int8_qk=True), dict(reweight=True, int8_qk=True, exact_kv_only=True),
+                   dict(reblock=True), dict(reblock=True, int8_qk=True, reweight=True)):
+        _route = dict(tau=0.7) if _i % 2 == 0 else dict(topk_ratio=0.3)
+        _COMBOS.append((dict(B=_B, N=_N, H=2, D=_D), dict(prefix_len=_pre, **_route, **_flags)))
+
+
+@pytest.mark.parametrize("shape,kw", _COMBOS, ids=[f"D{s['D']}_B{s['B']}_N{s['N']}_" + "_".join(
+    f"{k}" if v is True else f"{k}{v}" for k, v in kw.items()) for s, kw in _COMBOS])
+def test_mode_combinations(shape, kw):
+    """Every flag combination against the oracle on every output row: ragged
+    tails, B = 2, a prefix straddling a block and one covering all rows."""
+    q, k, v = inputs.iid(shape["B"], shape["N"], shape["H"], shape["D"], seed=shape["N"] + len(kw))
+    if kw.get("reblock"):
+        reblock_parity(q, k, v, **{a: b for a, b in kw.items() if a != "reblock"})
+    else:
+        full_parity(q, k, v, **kw)
