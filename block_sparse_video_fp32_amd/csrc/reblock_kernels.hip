@@ -15,8 +15,9 @@
 //                      that both operands are 16-byte LDS reads)
 //   gram_reduce_kernel M = sum of the partials, in chunk order
 //   embed_kernel       u_i = x_i / sqrt(x_i^T M x_i) and M u_i in bf16 (X M
-//                      on MFMA with M rounded to bf16; M is symmetric, so
-//                      its rows are the B operand) and the identity order
+//                      on MFMA with M rounded to bf16, M being symmetric so
+//                      that its rows are the B operand; x^T M x from the
+//                      bf16 X M) and the identity order
 //   split_kernel       one level of the partition, one workgroup per group:
 //                      the mean direction, the two pivots (least similar to
 //                      the mean, then least similar to the first pivot), the
@@ -152,20 +153,18 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(Shape s, Workspace ws)
 // ---------------------------------------------------------------------------
 // embed: grid (ceil(n_v / kEmbedRows), problems), 256 threads, 64 rows at a
 // time.  Y = X M on MFMA (M rounded to bf16; M is symmetric, so its rows are
-// the B operand); x^T M x = sum of X * Y over each tile's columns (shuffles)
-// and over the column tiles (in order).  Writes the unit rows
-// u = x / sqrt(x^T M x), the rows M u = Y / sqrt(x^T M x), both bf16, and the
-// identity order.
+// the B operand), stored as bf16 in LDS; four threads per row then take
+// x^T M x = x . y over their quarters of the row (two shuffles) and write the
+// unit row u = x / sqrt(x^T M x) and M u = y / sqrt(x^T M x), both bf16,
+// and the identity order.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void embed_kernel(Shape s, const uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ k, Workspace ws) {
-  constexpr int LP = D + 8, TW = D / 64, NK = D / 16;
+  constexpr int LP = D + 8, TW = D / 64, NK = D / 16, QD = D / 4;
   __shared__ __attribute__((aligned(16))) uint16_t Mb[D * LP];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kRbBlock * LP];
   __shared__ __attribute__((aligned(16))) uint16_t Ys[kRbBlock * LP];
-  __shared__ float part[D / 32][kRbBlock];
-  __shared__ float invs[kRbBlock];
   const int p = blockIdx.y;
   const Prob pr = prob_of(s, p);
   const uint16_t* x = rows_of(s, pr, q, k, false);
@@ -189,70 +188,62 @@ __global__ __launch_bounds__(256) void embed_kernel(Shape s, const uint16_t* __r
     }
   };
   if ((int)blockIdx.x * kEmbedRows < jend) fetch(blockIdx.x * kEmbedRows);
+  const int r = tid >> 2, qd = tid & 3;  // the row and quarter this thread finishes
   for (int j0 = blockIdx.x * kEmbedRows; j0 < jend; j0 += kRbBlock) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
-      const int i = tid + 256 * u, r = i / (D / 8), c8 = i % (D / 8);
-      *reinterpret_cast<uint4*>(Xs + r * LP + c8 * 8) = nxt[u];
+      const int i = tid + 256 * u, rr = i / (D / 8), c8 = i % (D / 8);
+      *reinterpret_cast<uint4*>(Xs + rr * LP + c8 * 8) = nxt[u];
     }
     __syncthreads();
     if (j0 + kRbBlock < jend) fetch(j0 + kRbBlock);
-    f32x16 acc[TW];
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
       const int ct = (w >> 1) * TW + t;
-      acc[t] = f32x16{};
+      f32x16 acc = {};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(Xs + (32 * rt + l32) * LP + 16 * kk + 8 * hh);
         const bf16x8 b = *reinterpret_cast<const bf16x8*>(Mb + (32 * ct + l32) * LP + 16 * kk + 8 * hh);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * rt + 8 * (i >> 2) + 4 * hh + (i & 3);
-        float v = acc[t][i] * bf(Xs[row * LP + 32 * ct + l32]);
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
-        if (l32 == 0) part[ct][row] = v;
-      }
+      for (int i = 0; i < 16; ++i)
+        Ys[(32 * rt + 8 * (i >> 2) + 4 * hh + (i & 3)) * LP + 32 * ct + l32] = (uint16_t)to_bf16(acc[i]);
     }
     __syncthreads();
-    const int r = tid >> 2, qd = tid & 3;
-    {
-      float n2 = 0.0f;
+    float xs[QD], ys[QD];
 #pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct) n2 += part[ct][r];
-      const float inv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
-      if (qd == 0) invs[r] = inv;
-      if (j0 + r < nv) {
+    for (int d = 0; d < QD; d += 8) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(Xs + r * LP + qd * QD + d);
+      const uint4 yv = *reinterpret_cast<const uint4*>(Ys + r * LP + qd * QD + d);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, yw[4] = {yv.x, yv.y, yv.z, yv.w};
 #pragma unroll
-        for (int d = qd * (D / 4); d < (qd + 1) * (D / 4); d += 8) {
-          uint32_t wd[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            wd[e] = to_bf16(bf(Xs[r * LP + d + 2 * e]) * inv) | (to_bf16(bf(Xs[r * LP + d + 2 * e + 1]) * inv) << 16);
-          *reinterpret_cast<uint4*>(U + (long long)(j0 + r) * D + d) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        }
-        if (qd == 0) ord0[j0 + r] = j0 + r;
+      for (int e = 0; e < 8; ++e) {
+        xs[d + e] = bf((xw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        ys[d + e] = bf((yw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
       }
     }
-    __syncthreads();
+    float n2 = 0.0f;
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      const int ct = (w >> 1) * TW + t;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * rt + 8 * (i >> 2) + 4 * hh + (i & 3);
-        Ys[row * LP + 32 * ct + l32] = (uint16_t)to_bf16(acc[t][i] * invs[row]);
-      }
-    }
-    __syncthreads();
+    for (int d = 0; d < QD; ++d) n2 += xs[d] * ys[d];
+    n2 += __shfl_xor(n2, 1);
+    n2 += __shfl_xor(n2, 2);
+    const float inv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
     if (j0 + r < nv) {
 #pragma unroll
-      for (int d = qd * (D / 4); d < (qd + 1) * (D / 4); d += 8)
-        *reinterpret_cast<uint4*>(MU + (long long)(j0 + r) * D + d) = *reinterpret_cast<const uint4*>(Ys + r * LP + d);
+      for (int d = 0; d < QD; d += 8) {
+        uint32_t wu[4], wm[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wu[e] = to_bf16(xs[d + 2 * e] * inv) | (to_bf16(xs[d + 2 * e + 1] * inv) << 16);
+          wm[e] = to_bf16(ys[d + 2 * e] * inv) | (to_bf16(ys[d + 2 * e + 1] * inv) << 16);
+        }
+        *reinterpret_cast<uint4*>(U + (long long)(j0 + r) * D + qd * QD + d) = make_uint4(wu[0], wu[1], wu[2], wu[3]);
+        *reinterpret_cast<uint4*>(MU + (long long)(j0 + r) * D + qd * QD + d) = make_uint4(wm[0], wm[1], wm[2], wm[3]);
+      }
+      if (qd == 0) ord0[j0 + r] = j0 + r;
     }
   }
 }
