@@ -94,6 +94,12 @@ int validate_params(const sparse_attn_params& p) {
                 SA_MAX_BLOCKS);
   if ((int64_t)p.B * p.H * nb > (int64_t)1 << 30)
     return fail(SA_EUNSUPPORTED_SHAPE, "B*H*n_b too large");
+  // grid y and z extents of the launches (at most 65535 each)
+  if (p.H > 65535 || (int64_t)p.B * ((p.H + 7) / 8) > 65535)
+    return fail(SA_EUNSUPPORTED_SHAPE, "B=%d, H=%d exceed the launch grid (H <= 65535, B*ceil(H/8) <= 65535)", p.B,
+                p.H);
+  if ((p.flags & SA_FLAG_REBLOCK) && 2 * (int64_t)p.B * p.H > 65535)
+    return fail(SA_EUNSUPPORTED_SHAPE, "SA_FLAG_REBLOCK needs 2*B*H <= 65535 (got B=%d, H=%d)", p.B, p.H);
   const bool in0 = p.in_stride_b == 0 && p.in_stride_t == 0 && p.in_stride_h == 0;
   const bool out0 = p.out_stride_b == 0 && p.out_stride_t == 0 && p.out_stride_h == 0;
   int rc;

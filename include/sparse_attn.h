@@ -105,7 +105,9 @@ extern "C" {
 /* Error codes. */
 #define SA_OK 0
 #define SA_EINVAL (-1)              /* null pointer, bad parameter value */
-#define SA_EUNSUPPORTED_SHAPE (-2)  /* D not 64/128, n_b > SA_MAX_BLOCKS, ... */
+#define SA_EUNSUPPORTED_SHAPE (-2)  /* D not 64/128, n_b > SA_MAX_BLOCKS, B*H*n_b > 2^30,
+                                       H > 65535, B*ceil(H/8) > 65535,
+                                       2*B*H > 65535 with SA_FLAG_REBLOCK */
 #define SA_EUNSUPPORTED_DEVICE (-3) /* current device is not gfx950 */
 #define SA_EWORKSPACE (-4)          /* workspace smaller than required */
 #define SA_EALIGN (-5)              /* pointer or stride not 16-byte aligned */

@@ -244,3 +244,13 @@ def test_workspace_bytes_and_route_entry_points(lib):
     n = ctypes.c_size_t()
     assert lib.sparse_attn_workspace_bytes(None, ctypes.byref(n)) == SA_EINVAL
     assert lib.sparse_attn_route(plan._h, None, None, None, None, 0, None) == SA_EINVAL
+
+
+def test_launch_grid_limits(lib):
+    """Shapes whose launch grids would exceed 65535 in y or z are refused at
+    plan time with SA_EUNSUPPORTED_SHAPE (never at launch)."""
+    assert _create(lib, _params(B=1, N=64, H=70000)) == SA_EUNSUPPORTED_SHAPE
+    assert _create(lib, _params(B=70000, N=64, H=8)) == SA_EUNSUPPORTED_SHAPE
+    assert _create(lib, _params(B=1, N=64, H=40000)) == 0
+    assert _create(lib, _params(B=1, N=64, H=40000, flags=3 | 32)) == SA_EUNSUPPORTED_SHAPE
+    assert "REBLOCK" in lib.sparse_attn_last_error().decode()
