@@ -2,11 +2,16 @@
 //
 //   pool_q_kernel  per-64-row-block means of Q in FP32 (HBM-bound stream;
 //                  Star7 README, 工作原理 > Sol: Q64/K64 blocks).
+//   anchor_kernel  Spark-Reweight only: the mean of a head's video query
+//                  rows, from the block means (Spark-H3 news, Spark-Reweight).
 //   pack_kv_kernel per block of one head: the FP32 means of K and V (the
 //                  centroids; Spark-H3 news, Spark-Reweight: mean-pooled K/V
 //                  summaries), plus K, V^T and the centroids rewritten in the
 //                  register order of the attend kernel's MFMA operands, so
-//                  that every operand load there is one coalesced 1 KB read.
+//                  that every operand load there is one coalesced 1 KB read;
+//                  optionally the anchor-weighted centroids and their bias
+//                  (Spark-Reweight) or the INT8 residual codes of K
+//                  (thakicloud accel-stack post, measured results).
 //   select_kernel  fp32 block scores Qbar_a . Kbar_c for a group of query
 //                  blocks against every key block, then per query block
 //                  (one wave each) the threshold mean + tau * std (two-pass,
@@ -21,7 +26,8 @@
 //                  unselected block with the log-mass bias, all merged into
 //                  the same FP32 softmax (Star7 README, Sol: missed blocks
 //                  contribute through a K/V centroid in the same FP32 online
-//                  softmax).
+//                  softmax).  Template instances add the reweight bias and
+//                  INT8 QK^T without touching the default instance.
 //
 // Packed operand layouts (bf16).  A "half tile" is 32 keys x D, stored as
 // D/16 blocks of 64 lanes x 8 elements (1 KB at D = 128); kappa(r) is r with

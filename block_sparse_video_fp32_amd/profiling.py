@@ -64,8 +64,16 @@ def counter_per_dispatch(dirname: str, counter: str, kernel_substr: str):
 
 
 def kernel_source_hash() -> str:
-    with open(os.path.join(HERE, "csrc", "sparse_attn_kernels.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attend kernel's source file without comment lines, end of
+    line comments and blank lines, so that edits of comments alone do not
+    mark the recorded counters as stale."""
+    lines = []
+    with open(os.path.join(HERE, "csrc", "sparse_attn_kernels.hip"), encoding="utf-8") as f:
+        for line in f:
+            code = line.split("//", 1)[0].rstrip()
+            if code.strip():
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int):
