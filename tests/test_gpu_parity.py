@@ -739,3 +739,46 @@ def test_mode_combinations(shape, kw):
         reblock_parity(q, k, v, **{a: b for a, b in kw.items() if a != "reblock"})
     else:
         full_parity(q, k, v, **kw)
+
+
+def test_workload_h3_reblock_reweight_int8_sampled():
+    """h3 (N = 38247, 1024 prefix rows, top-K 0.1, ragged tail, a 10-level
+    tree) with reblock, reweight and INT8 QK^T together: orders valid and
+    prefix fixed, every split of two heads per side against the oracle, lists,
+    and sampled output blocks against the oracle on the GPU's orders."""
+    w = inputs.make_workload("h3")
+    kw = dict(topk_ratio=w.topk_ratio, prefix_len=w.prefix_len, reweight=True, int8_qk=True)
+    run = GpuRun(w.q, w.k, w.v, reblock=True, **kw)
+    M, U, MU, pq, pk = run.plan.reblock_views(run.ws)
+    M = M.cpu().numpy().astype(np.float64)
+    pq, pk = pq.cpu().numpy(), pk.cpu().numpy()
+    B, N, H, D = w.shape
+    r0 = min(O.prefix_blocks(w.prefix_len) * 64, N)
+    assert run.plan.layout["reblock_levels"] == 10
+    n_split = 0
+    for side, perm in enumerate((pq, pk)):
+        for h in range(H):
+            assert (perm[0, h, :r0] == np.arange(r0)).all()
+            assert np.array_equal(np.sort(perm[0, h]), np.arange(N))
+        for h in (7, 41):
+            ug = U[side, 0, h].float().cpu().numpy().astype(np.float64)
+            mug = MU[side, 0, h].float().cpu().numpy().astype(np.float64)
+            n_split += check_reblock_splits(ug, M[side, 0, h], perm[0, h, r0:] - r0, MU=mug)
+    print(f"  h3 reblock: {n_split} splits validated", flush=True)
+    qf, kf, vf = _f32(w.q), _f32(w.k), _f32(w.v)
+    qp, kp, vp = _permute(qf, pq), _permute(kf, pk), _permute(vf, pk)
+    okw = oracle_kw(kw)
+    _, info = O.forward_blocks(qp, kp, vp, [], **okw)
+    sel = run.selection()
+    check_route(sel, info)
+    nb = O.num_blocks(N)
+    rng = np.random.default_rng(5)
+    blocks = sorted({(0, int(rng.integers(H)), int(rng.integers(nb))) for _ in range(16)}
+                    | {(0, 0, nb - 1), (0, 3, 0), (0, 5, 15), (0, 6, 16)})
+    parts, _ = O.forward_blocks(qp, kp, vp, blocks, info=dict(info, sel=sel), **okw)
+    got = run.out_f64()
+    g, r = [], []
+    for (b, h, a), o in parts.items():
+        g.append(got[b, pq[b, h, a * 64 : a * 64 + o.shape[0]], h])
+        r.append(o)
+    check_output(np.concatenate(g), np.concatenate(r), f"h3 reblock+reweight+int8 ({len(parts)} blocks)")
