@@ -21,6 +21,9 @@
  *      block's valid row count (log-mass bias, "Spark-H3" news,
  *      Spark-Reweight bullet); both kinds of term share one FP32 online
  *      softmax.
+ * Optional modes (flags, each documented at its definition): Spark-Reweight
+ * centroids (SA_FLAG_REWEIGHT), INT8 QK^T on the exact blocks
+ * (SA_FLAG_INT8_QK) and the Spark-Reblock partition (SA_FLAG_REBLOCK).
  *
  * Tensors are bf16 in the BTHD layout [B, N, H, D] with D contiguous (the
  * layout of the aikraft.ru RTX 5090 table), D in {64, 128}.  A ragged last
@@ -217,7 +220,9 @@ int sparse_attn_workspace_layout(const sparse_attn_plan* plan, sparse_attn_ws_la
 int sparse_attn_workspace_bytes(const sparse_attn_plan* plan, size_t* bytes);
 
 /* Full forward: pool, select and attend (pool and attend alone on the dense
- * path) enqueued on `stream` (a hipStream_t; NULL is the null stream).
+ * path) enqueued on `stream` (a hipStream_t; NULL is the null stream); with
+ * SA_FLAG_REBLOCK, first the partition and the reordered copies of q, k, v
+ * in ws, then the same steps on them, then the output rows put back.
  * q, k, v are read-only bf16 device pointers and may alias one another; out
  * is a bf16 device pointer that must not overlap them or ws.  ws points to at
  * least layout.total_bytes of device memory (256-byte aligned), ws_bytes is
@@ -226,7 +231,9 @@ int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void*
                         void* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Step 1 alone: block means of Q, K, V and the packed K, V^T and centroid
- * tiles (every section listed under "After sparse_attn_pool"). */
+ * tiles (every section listed under "After sparse_attn_pool").  The stage
+ * calls (pool, select, route, attend) refuse a SA_FLAG_REBLOCK plan with
+ * SA_EINVAL: its steps run through sparse_attn_forward only. */
 int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
                      void* ws, size_t ws_bytes, void* stream);
 
