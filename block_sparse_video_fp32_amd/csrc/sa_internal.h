@@ -66,6 +66,7 @@ struct Workspace {
   uint16_t* rb_k;
   uint16_t* rb_v;
   uint16_t* rb_out;
+  int* pair_order;  // [B,H,ceil(nb/2)] pairs of each (b, h), longest lists first
 };
 
 hipError_t launch_pool_q(const Shape& s, const void* q, const Workspace& ws, hipStream_t stream);

@@ -18,6 +18,7 @@ struct sparse_attn_plan {
   sparse_attn_params params;
   sa::Shape shape;
   sparse_attn_ws_layout layout;
+  uint64_t order_off;  // attend dispatch order (after the public sections)
 };
 
 namespace {
@@ -208,6 +209,7 @@ void build_plan(sparse_attn_plan* pl) {
   L.rb_keys = off; off = align256(off + rb * P * s.rb_n * sizeof(uint32_t));
   L.rb_qkv = off; off = align256(off + rb * 3 * qkv);
   L.rb_out = off; off = align256(off + rb * qkv);
+  pl->order_off = off; off = align256(off + bh * (uint64_t)((s.nb + 1) / 2) * sizeof(int32_t));
   L.total_bytes = off;
   L.n_blocks = s.nb;
   L.n_blocks_padded = s.nbp;
@@ -246,6 +248,7 @@ sa::Workspace carve(const sparse_attn_plan* pl, void* ws) {
   w.rb_k = w.rb_q + qkv;
   w.rb_v = w.rb_k + qkv;
   w.rb_out = reinterpret_cast<uint16_t*>(base + L.rb_out);
+  w.pair_order = reinterpret_cast<int*>(base + pl->order_off);
   return w;
 }
 

@@ -28,6 +28,9 @@
 //                  contribute through a K/V centroid in the same FP32 online
 //                  softmax).  Template instances add the reweight bias and
 //                  INT8 QK^T without touching the default instance.
+//   pair_order_kernel  the order in which the attend workgroups of one
+//                  (b, h) take its pairs: longest lists first, so that the
+//                  shortest run last and the launch drains sooner.
 //
 // Packed operand layouts (bf16).  A "half tile" is 32 keys x D, stored as
 // D/16 blocks of 64 lanes x 8 elements (1 KB at D = 128); kappa(r) is r with
@@ -845,8 +848,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Q8 ? 2 : 3,
   const int nb = s.nb, N = s.N;
   const float c1 = s.c1;
   const int np = (nb + 1) >> 1;
-  const int p = lid % np;
   const int bhi = lid / np;
+  const int p = s.dense ? lid % np : min(max(ws.pair_order[(long long)bhi * np + lid % np], 0), np - 1);
   const int h = bhi % s.H, b = bhi / s.H;
   const long long bh = bhi;
   const int a0 = 2 * p;
@@ -1267,6 +1270,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Q8 ? 2 : 3,
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// pair_order: grid B H, 256 threads.  The attend workgroups of one (b, h)
+// take its pairs of query blocks longest first (by the two list lengths,
+// ties by position), so that the shortest ones run last and the end of the
+// launch drains sooner.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pair_order_kernel(Shape s, Workspace ws) {
+  __shared__ int len[SA_MAX_BLOCKS / 2];
+  const long long bh = blockIdx.x;
+  const int nb = s.nb, np = (nb + 1) >> 1;
+  for (int p = threadIdx.x; p < np; p += 256) {
+    const int a = 2 * p;
+    int l = min(max(ws.counts[bh * nb + a], 0), nb);
+    if (a + 1 < nb) l += min(max(ws.counts[bh * nb + a + 1], 0), nb);
+    len[p] = l;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < np; p += 256) {
+    const int l = len[p];
+    int rank = 0;
+    for (int r = 0; r < np; ++r) {
+      const int lr = len[r];
+      rank += (lr > l || (lr == l && r < p)) ? 1 : 0;
+    }
+    ws.pair_order[bh * np + rank] = p;
+  }
+}
+
 // Ring depth: half tile u + 1 is requested while u is computed.  At
 // N = 16384 and 32768, 2, 3 and 4 stages ran within 1% of each other at the
 // same occupancy; two stages (32 KB at D = 128) let three workgroups share a
@@ -1280,6 +1312,11 @@ hipError_t launch_attend_t(const Shape& s, const uint16_t* q, uint16_t* out, con
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, S, RW, Q8>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
+  if (!s.dense) {
+    hipLaunchKernelGGL(pair_order_kernel, dim3((unsigned)(s.B * s.H)), dim3(256), 0, stream, s, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dim3 grid((unsigned)((long long)s.B * s.H * ((s.nb + 1) / 2)));
   hipLaunchKernelGGL((attend_kernel<D, S, RW, Q8>), grid, dim3(256), bytes, stream, s, q, out, ws);
   return hipGetLastError();
