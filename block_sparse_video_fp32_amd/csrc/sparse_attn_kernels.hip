@@ -464,11 +464,17 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
       qa[j + 3] = x.w;
     }
   }
-  auto load_kb = [&](int c, float (&kb)[KS]) {
+  // Kbar fragments in chunks of 8 k-steps, software-pipelined: the next
+  // chunk (after the last one, the first chunk of the next pair of key
+  // tiles) is requested before the current chunk's MFMAs, so the loads of
+  // a wave overlap its own MFMAs.  The k-step order of each accumulator is
+  // unchanged.
+  constexpr int CH = 8, NCH = KS / CH;
+  auto load_chunk = [&](int c, int ch, float (&kb)[CH]) {
 #pragma unroll
-    for (int j = 0; j < KS; j += 4) {
+    for (int j = 0; j < CH; j += 4) {
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c < nb) x = *reinterpret_cast<const float4*>(kbar + (long long)c * D + KS * g + j);
+      if (c < nb) x = *reinterpret_cast<const float4*>(kbar + (long long)c * D + KS * g + CH * ch + j);
       kb[j] = x.x;
       kb[j + 1] = x.y;
       kb[j + 2] = x.z;
@@ -477,21 +483,34 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
   };
   // Wave w takes the key tiles of 16 blocks at 32 w + 128 t and 32 w + 128 t + 16
   // (two independent accumulator chains).
-  for (int c0 = 32 * w; c0 < nb; c0 += 128) {
-    float kb0[KS], kb1[KS];
-    load_kb(c0 + l16, kb0);
-    load_kb(c0 + 16 + l16, kb1);
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (32 * w < nb) {
+    float b0[2][CH], b1[2][CH];
+    load_chunk(32 * w + l16, 0, b0[0]);
+    load_chunk(32 * w + 16 + l16, 0, b1[0]);
+    for (int c0 = 32 * w; c0 < nb; c0 += 128) {
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j], kb0[j], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[j], kb1[j], acc1, 0, 0, 0);
-    }
-    // accumulator lane l, register i: row 4 (l/16) + i, key c + l%16
+      for (int ch = 0; ch < NCH; ++ch) {
+        const int cur = ch & 1;
+        if (ch + 1 < NCH) {
+          load_chunk(c0 + l16, ch + 1, b0[cur ^ 1]);
+          load_chunk(c0 + 16 + l16, ch + 1, b1[cur ^ 1]);
+        } else if (c0 + 128 < nb) {
+          load_chunk(c0 + 128 + l16, 0, b0[cur ^ 1]);
+          load_chunk(c0 + 144 + l16, 0, b1[cur ^ 1]);
+        }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (c0 + l16 < nb) S[(4 * g + i) * nb + c0 + l16] = acc0[i];
-      if (c0 + 16 + l16 < nb) S[(4 * g + i) * nb + c0 + 16 + l16] = acc1[i];
+        for (int j = 0; j < CH; ++j) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[CH * ch + j], b0[cur][j], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[CH * ch + j], b1[cur][j], acc1, 0, 0, 0);
+        }
+      }
+      // accumulator lane l, register i: row 4 (l/16) + i, key c + l%16
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (c0 + l16 < nb) S[(4 * g + i) * nb + c0 + l16] = acc0[i];
+        if (c0 + 16 + l16 < nb) S[(4 * g + i) * nb + c0 + 16 + l16] = acc1[i];
+      }
     }
   }
   __syncthreads();
