@@ -58,6 +58,13 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte store that bypasses cache retention: the packed tiles are written
+// once here and read back by later launches from HBM either way.
+__device__ __forceinline__ void store_stream(void* dst, uint32_t x, uint32_t y, uint32_t z, uint32_t w) {
+  __builtin_nontemporal_store(u32x4{x, y, z, w}, reinterpret_cast<u32x4*>(dst));
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -378,7 +385,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
           wd[jj >> 2] |= ((uint32_t)code & 0xffu) << (8 * (jj & 3));
         }
       }
-      *reinterpret_cast<uint4*>(k8 + (long long)o * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      store_stream(k8 + (long long)o * 16, wd[0], wd[1], wd[2], wd[3]);
     }
   }
 
@@ -392,7 +399,8 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
       // K: chunk (m, l) = K[kappa(l % 32)][16 m + 8 (l / 32) .. +8]
       const int row = 32 * ht + kappa(l & 31);
       const int d0 = 16 * m + 8 * (l >> 5);
-      *reinterpret_cast<uint4*>(kp + (long long)o * 8) = *reinterpret_cast<const uint4*>(Kl + row * LS + d0);
+      const uint4 t4 = *reinterpret_cast<const uint4*>(Kl + row * LS + d0);
+      store_stream(kp + (long long)o * 8, t4.x, t4.y, t4.z, t4.w);
     }
     {
       // V^T: chunk (m = 2 dt + jj, l) = V[vt_key(jj, l, e)][32 dt + l % 32], e = 0..7
@@ -404,7 +412,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
         const uint32_t hi = Vl[(32 * ht + vt_key(jj, l, 2 * e2 + 1)) * LS + d];
         w[e2] = lo | (hi << 16);
       }
-      *reinterpret_cast<uint4*>(vp + (long long)o * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+      store_stream(vp + (long long)o * 8, w[0], w[1], w[2], w[3]);
     }
   }
 }
