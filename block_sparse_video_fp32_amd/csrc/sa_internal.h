@@ -67,6 +67,8 @@ struct Workspace {
   uint16_t* rb_v;
   uint16_t* rb_out;
   int* pair_order;  // [B,H,ceil(nb/2)] pairs of each (b, h), longest lists first
+  int* head_work;   // [B,H] total list length of each (b, h)
+  int* head_order;  // [B,H] (b, h) of each head slot, balanced over the XCDs
 };
 
 hipError_t launch_pool_q(const Shape& s, const void* q, const Workspace& ws, hipStream_t stream);

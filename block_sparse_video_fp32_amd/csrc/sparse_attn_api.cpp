@@ -209,7 +209,7 @@ void build_plan(sparse_attn_plan* pl) {
   L.rb_keys = off; off = align256(off + rb * P * s.rb_n * sizeof(uint32_t));
   L.rb_qkv = off; off = align256(off + rb * 3 * qkv);
   L.rb_out = off; off = align256(off + rb * qkv);
-  pl->order_off = off; off = align256(off + bh * (uint64_t)((s.nb + 1) / 2) * sizeof(int32_t));
+  pl->order_off = off; off = align256(off + (bh * (uint64_t)((s.nb + 1) / 2) + 2 * bh) * sizeof(int32_t));
   L.total_bytes = off;
   L.n_blocks = s.nb;
   L.n_blocks_padded = s.nbp;
@@ -249,6 +249,9 @@ sa::Workspace carve(const sparse_attn_plan* pl, void* ws) {
   w.rb_v = w.rb_k + qkv;
   w.rb_out = reinterpret_cast<uint16_t*>(base + L.rb_out);
   w.pair_order = reinterpret_cast<int*>(base + pl->order_off);
+  const uint64_t nbh = (uint64_t)pl->params.B * pl->params.H;
+  w.head_work = w.pair_order + nbh * (uint64_t)((pl->shape.nb + 1) / 2);
+  w.head_order = w.head_work + nbh;
   return w;
 }
 

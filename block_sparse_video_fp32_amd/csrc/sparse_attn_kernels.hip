@@ -31,6 +31,9 @@
 //   pair_order_kernel  the order in which the attend workgroups of one
 //                  (b, h) take its pairs: longest lists first, so that the
 //                  shortest run last and the launch drains sooner.
+//   head_order_kernel  which heads each XCD's run of attend workgroups
+//                  serves: dealt in snake order of decreasing total list
+//                  length, so that the XCDs finish together.
 //
 // Packed operand layouts (bf16).  A "half tile" is 32 keys x D, stored as
 // D/16 blocks of 64 lanes x 8 elements (1 KB at D = 128); kappa(r) is r with
@@ -647,6 +650,10 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
 // so P^T goes from accumulator to operand with no lane movement, and every
 // LDS read is a linear, conflict-free ds_read_b128.
 // ---------------------------------------------------------------------------
+// Heads ordered across the XCDs only up to this many (the ordering takes
+// O((B H)^2) comparisons in one workgroup).
+constexpr int kMaxOrderedHeads = 4096;
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -875,7 +882,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Q8 ? 2 : 3,
   const int nb = s.nb, N = s.N;
   const float c1 = s.c1;
   const int np = (nb + 1) >> 1;
-  const int bhi = lid / np;
+  const int nbh = s.B * s.H;
+  const int bhi = (s.dense || (nbh & 7) || nbh > kMaxOrderedHeads) ? lid / np
+                                                           : min(max(ws.head_order[lid / np], 0), nbh - 1);
   const int p = s.dense ? lid % np : min(max(ws.pair_order[(long long)bhi * np + lid % np], 0), np - 1);
   const int h = bhi % s.H, b = bhi / s.H;
   const long long bh = bhi;
@@ -1315,14 +1324,43 @@ __global__ __launch_bounds__(256) void pair_order_kernel(Shape s, Workspace ws) 
     len[p] = l;
   }
   __syncthreads();
+  int tot = 0;
   for (int p = threadIdx.x; p < np; p += 256) {
     const int l = len[p];
+    tot += l;
     int rank = 0;
     for (int r = 0; r < np; ++r) {
       const int lr = len[r];
       rank += (lr > l || (lr == l && r < p)) ? 1 : 0;
     }
     ws.pair_order[bh * np + rank] = p;
+  }
+  // the head's total list length (its work), for head_order_kernel
+  __shared__ int part[4];
+  tot = (int)wave_sum((float)tot);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = tot;
+  __syncthreads();
+  if (threadIdx.x == 0) ws.head_work[bh] = part[0] + part[1] + part[2] + part[3];
+}
+
+// ---------------------------------------------------------------------------
+// head_order: one workgroup, 256 threads.  The attend launch gives each XCD
+// a contiguous run of B H / 8 heads; the heads are dealt to the eight runs
+// in snake order of decreasing work (0..7, 7..0, ...), so that every XCD
+// gets about the same total.  Used when B H is a multiple of 8.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void head_order_kernel(int nbh, Workspace ws) {
+  const int per = nbh / 8;
+  for (int h = threadIdx.x; h < nbh; h += 256) {
+    const int wk = ws.head_work[h];
+    int rank = 0;
+    for (int r = 0; r < nbh; ++r) {
+      const int wr = ws.head_work[r];
+      rank += (wr > wk || (wr == wk && r < h)) ? 1 : 0;
+    }
+    const int round = rank / 8, pos = rank % 8;
+    const int xcd = (round & 1) ? 7 - pos : pos;
+    ws.head_order[xcd * per + round] = h;
   }
 }
 
@@ -1343,6 +1381,12 @@ hipError_t launch_attend_t(const Shape& s, const uint16_t* q, uint16_t* out, con
     hipLaunchKernelGGL(pair_order_kernel, dim3((unsigned)(s.B * s.H)), dim3(256), 0, stream, s, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int nbh = s.B * s.H;
+    if (!(nbh & 7) && nbh <= kMaxOrderedHeads) {
+      hipLaunchKernelGGL(head_order_kernel, dim3(1), dim3(256), 0, stream, nbh, ws);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   dim3 grid((unsigned)((long long)s.B * s.H * ((s.nb + 1) / 2)));
   hipLaunchKernelGGL((attend_kernel<D, S, RW, Q8>), grid, dim3(256), bytes, stream, s, q, out, ws);

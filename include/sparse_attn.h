@@ -137,7 +137,8 @@ typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
 /* Byte offsets of the workspace sections (all 256-byte aligned; a section
  * a plan does not use has size 0).  total_bytes also covers a last,
  * unlisted scratch section that sparse_attn_attend rewrites on every routed
- * call (the order in which each (b, h)'s pairs of query blocks run).
+ * call (the order in which the heads and each (b, h)'s pairs of query blocks
+ * run).
  *
  * After sparse_attn_pool:
  *   qbar, kbar, vbar  fp32 [B, H, n_b, D]: the block means of Q, K, V.
