@@ -650,10 +650,6 @@ __global__ __launch_bounds__(256) void select_kernel(Shape s, Workspace ws) {
 // so P^T goes from accumulator to operand with no lane movement, and every
 // LDS read is a linear, conflict-free ds_read_b128.
 // ---------------------------------------------------------------------------
-// Heads ordered across the XCDs only up to this many (the ordering takes
-// O((B H)^2) comparisons in one workgroup).
-constexpr int kMaxOrderedHeads = 4096;
-
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -854,6 +850,10 @@ __device__ __forceinline__ void tile_pv(const uint8_t* stage, int vblk, int lane
   __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
 }
+
+// Heads ordered across the XCDs only up to this many (the ordering takes
+// O((B H)^2) comparisons in one workgroup).
+constexpr int kMaxOrderedHeads = 4096;
 
 template <int D, int S, bool RW, bool Q8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Q8 ? 2 : 3, Q8 ? 2 : 3))) void attend_kernel(
@@ -1337,7 +1337,8 @@ __global__ __launch_bounds__(256) void pair_order_kernel(Shape s, Workspace ws) 
   }
   // the head's total list length (its work), for head_order_kernel
   __shared__ int part[4];
-  tot = (int)wave_sum((float)tot);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = tot;
   __syncthreads();
   if (threadIdx.x == 0) ws.head_work[bh] = part[0] + part[1] + part[2] + part[3];
