@@ -24,8 +24,8 @@
 //                      rank values (M u_j) . (u_b - u_a), an exact radix
 //                      select of the left child's size (ties by position)
 //                      and a stable two-way partition of the group's order
-//   gather / scatter   Q, K, V rows into the new orders (contiguous copies
-//                      in the workspace) and the output rows back
+// The path then reads Q, K, V rows through the final orders and writes each
+// output row at its own position (no reordered copies).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -553,48 +553,6 @@ __global__ __launch_bounds__(NT) void split_kernel(Shape s, int level, Workspace
   }
 }
 
-// ---------------------------------------------------------------------------
-// gather: grid (N, B), 256 threads.  Row i of the reordered Q (K, V) is row
-// perm(i) of the input: i itself in the prefix blocks, else the final order.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int perm_row(const Shape& s, const int* ord, int p, int i) {
-  return (i < s.rb_r0) ? i : s.rb_r0 + ord[(long long)p * s.rb_n + (i - s.rb_r0)];
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void gather_kernel(Shape s, const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ k,
-                                                     const uint16_t* __restrict__ v, Workspace ws) {
-  constexpr int CPR = D / 8;
-  const int i = blockIdx.x, b = blockIdx.y, BH = s.B * s.H;
-  const int* ord = ws.rb_ord + (long long)(s.rb_levels & 1) * s.rb_P * s.rb_n;
-  const int per = s.H * CPR;
-  for (int c = threadIdx.x; c < 3 * per; c += 256) {
-    const int tsel = c / per, rem = c % per, h = rem / CPR, c8 = rem % CPR;
-    const int side = tsel == 0 ? 0 : 1;
-    const int src = perm_row(s, ord, side * BH + b * s.H + h, i);
-    const uint16_t* base = tsel == 0 ? q : (tsel == 1 ? k : v);
-    uint16_t* dst = tsel == 0 ? ws.rb_q : (tsel == 1 ? ws.rb_k : ws.rb_v);
-    const uint4 x = *reinterpret_cast<const uint4*>(base + (long long)b * s.isb + (long long)src * s.ist +
-                                                    (long long)h * s.ish + c8 * 8);
-    *reinterpret_cast<uint4*>(dst + (((long long)b * s.N + i) * s.H + h) * D + c8 * 8) = x;
-  }
-}
-
-// scatter: grid (N, B).  Output row perm_q(i) <- row i of the reordered output.
-template <int D>
-__global__ __launch_bounds__(256) void scatter_kernel(Shape s, uint16_t* __restrict__ out, Workspace ws) {
-  constexpr int CPR = D / 8;
-  const int i = blockIdx.x, b = blockIdx.y;
-  const int* ord = ws.rb_ord + (long long)(s.rb_levels & 1) * s.rb_P * s.rb_n;
-  for (int c = threadIdx.x; c < s.H * CPR; c += 256) {
-    const int h = c / CPR, c8 = c % CPR;
-    const int dst = perm_row(s, ord, b * s.H + h, i);
-    const uint4 x = *reinterpret_cast<const uint4*>(ws.rb_out + (((long long)b * s.N + i) * s.H + h) * D + c8 * 8);
-    *reinterpret_cast<uint4*>(out + (long long)b * s.osb + (long long)dst * s.ost + (long long)h * s.osh + c8 * 8) = x;
-  }
-}
-
 template <int D>
 hipError_t partition_t(const Shape& s, const uint16_t* q, const uint16_t* k, const Workspace& ws,
                        hipStream_t stream) {
@@ -625,25 +583,5 @@ hipError_t launch_reblock_partition(const Shape& s, const void* q, const void* k
   return partition_t<64>(s, qq, kk, ws, stream);
 }
 
-hipError_t launch_reblock_gather(const Shape& s, const void* q, const void* k, const void* v, const Workspace& ws,
-                                 hipStream_t stream) {
-  const auto* qq = static_cast<const uint16_t*>(q);
-  const auto* kk = static_cast<const uint16_t*>(k);
-  const auto* vv = static_cast<const uint16_t*>(v);
-  if (s.D == 128)
-    hipLaunchKernelGGL(gather_kernel<128>, dim3(s.N, s.B), dim3(256), 0, stream, s, qq, kk, vv, ws);
-  else
-    hipLaunchKernelGGL(gather_kernel<64>, dim3(s.N, s.B), dim3(256), 0, stream, s, qq, kk, vv, ws);
-  return hipGetLastError();
-}
-
-hipError_t launch_reblock_scatter(const Shape& s, void* out, const Workspace& ws, hipStream_t stream) {
-  auto* oo = static_cast<uint16_t*>(out);
-  if (s.D == 128)
-    hipLaunchKernelGGL(scatter_kernel<128>, dim3(s.N, s.B), dim3(256), 0, stream, s, oo, ws);
-  else
-    hipLaunchKernelGGL(scatter_kernel<64>, dim3(s.N, s.B), dim3(256), 0, stream, s, oo, ws);
-  return hipGetLastError();
-}
 
 }  // namespace sa

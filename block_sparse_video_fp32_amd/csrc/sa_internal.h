@@ -39,6 +39,8 @@ struct Shape {
   int rb_levels;            // levels of the split tree
   int rb_chunks;            // partial second moments per problem
   int rb_P;                 // problems: 2 sides x B x H
+  int permuted;             // the path reads Q, K, V rows (and writes output
+                            // rows) through the final reblock orders
 };
 
 // Device workspace sections (see the layout notes in sparse_attn.h).
@@ -62,10 +64,6 @@ struct Workspace {
   uint16_t* rb_MU; // [P, rb_n, D] bf16 M u of the unit rows
   int* rb_ord;     // [2, P, rb_n] orders (ping-pong by level)
   uint32_t* rb_key;  // [P, rb_n] rank keys
-  uint16_t* rb_q;  // [B, N, H, D] reordered copies and output
-  uint16_t* rb_k;
-  uint16_t* rb_v;
-  uint16_t* rb_out;
   int* pair_order;  // [B,H,ceil(nb/2)] pairs of each (b, h), longest lists first
   int* head_work;   // [B,H] total list length of each (b, h)
   int* head_order;  // [B,H] (b, h) of each head slot, balanced over the XCDs
@@ -78,9 +76,6 @@ hipError_t launch_pack_kv(const Shape& s, const void* k, const void* v, const Wo
 hipError_t launch_select(const Shape& s, const Workspace& ws, hipStream_t stream);
 hipError_t launch_reblock_partition(const Shape& s, const void* q, const void* k, const Workspace& ws,
                                     hipStream_t stream);
-hipError_t launch_reblock_gather(const Shape& s, const void* q, const void* k, const void* v, const Workspace& ws,
-                                 hipStream_t stream);
-hipError_t launch_reblock_scatter(const Shape& s, void* out, const Workspace& ws, hipStream_t stream);
 hipError_t launch_attend(const Shape& s, const void* q, void* out, const Workspace& ws,
                          hipStream_t stream);
 

@@ -178,6 +178,7 @@ void build_plan(sparse_attn_plan* pl) {
   for (int m = (s.rb_n + sa::kBlock - 1) / sa::kBlock; (1 << s.rb_levels) < m;) ++s.rb_levels;
   s.rb_chunks = (p.N + sa::kGramChunk - 1) / sa::kGramChunk;
   s.rb_P = 2 * p.B * p.H;
+  s.permuted = 0;
 
   sparse_attn_ws_layout& L = pl->layout;
   std::memset(&L, 0, sizeof(L));
@@ -200,15 +201,16 @@ void build_plan(sparse_attn_plan* pl) {
   L.k_int8 = off; off = align256(off + (s.int8 ? bh * s.nb * 64ull * p.D : 0));
   L.kbase = off; off = align256(off + (s.int8 ? bh * s.nb * (uint64_t)(p.D + 8) * sizeof(uint16_t) : 0));
   const uint64_t rb = s.reblock ? 1 : 0;
-  const uint64_t P = 2 * bh, dd = (uint64_t)p.D * p.D, qkv = bh * (uint64_t)p.N * p.D * sizeof(uint16_t);
+  const uint64_t P = 2 * bh, dd = (uint64_t)p.D * p.D;
   L.rb_gram = off; off = align256(off + rb * P * s.rb_chunks * dd * sizeof(float));
   L.rb_metric = off; off = align256(off + rb * P * dd * sizeof(float));
   L.rb_units = off; off = align256(off + rb * P * s.rb_n * (uint64_t)p.D * sizeof(uint16_t));
   L.rb_munits = off; off = align256(off + rb * P * s.rb_n * (uint64_t)p.D * sizeof(uint16_t));
   L.rb_order = off; off = align256(off + rb * 2 * P * s.rb_n * sizeof(int32_t));
   L.rb_keys = off; off = align256(off + rb * P * s.rb_n * sizeof(uint32_t));
-  L.rb_qkv = off; off = align256(off + rb * 3 * qkv);
-  L.rb_out = off; off = align256(off + rb * qkv);
+  // rb_qkv, rb_out: no reordered copies (the path reads through the orders)
+  L.rb_qkv = off;
+  L.rb_out = off;
   pl->order_off = off; off = align256(off + (bh * (uint64_t)((s.nb + 1) / 2) + 2 * bh) * sizeof(int32_t));
   L.total_bytes = off;
   L.n_blocks = s.nb;
@@ -243,11 +245,6 @@ sa::Workspace carve(const sparse_attn_plan* pl, void* ws) {
   w.rb_MU = reinterpret_cast<uint16_t*>(base + L.rb_munits);
   w.rb_ord = reinterpret_cast<int*>(base + L.rb_order);
   w.rb_key = reinterpret_cast<uint32_t*>(base + L.rb_keys);
-  const uint64_t qkv = (uint64_t)pl->params.B * pl->params.N * pl->params.H * pl->params.D;
-  w.rb_q = reinterpret_cast<uint16_t*>(base + L.rb_qkv);
-  w.rb_k = w.rb_q + qkv;
-  w.rb_v = w.rb_k + qkv;
-  w.rb_out = reinterpret_cast<uint16_t*>(base + L.rb_out);
   w.pair_order = reinterpret_cast<int*>(base + pl->order_off);
   const uint64_t nbh = (uint64_t)pl->params.B * pl->params.H;
   w.head_work = w.pair_order + nbh * (uint64_t)((pl->shape.nb + 1) / 2);
@@ -385,20 +382,11 @@ int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void*
   const sa::Workspace w = carve(plan, ws);
   hipStream_t st = (hipStream_t)stream;
   sa::Shape s = plan->shape;
-  void* o = out;
   if (s.reblock) {
-    // partition, reorder Q, K, V into contiguous copies, run the path on
-    // them, and put the output rows back
+    // the partition; the path then reads its rows through the final orders
+    // and writes every output row at its own position
     if ((rc = launched(sa::launch_reblock_partition(s, q, k, w, st), "reblock partition"))) return rc;
-    if ((rc = launched(sa::launch_reblock_gather(s, q, k, v, w, st), "reblock gather"))) return rc;
-    const long long hd = (long long)s.H * s.D;
-    s.isb = s.osb = hd * s.N;
-    s.ist = s.ost = hd;
-    s.ish = s.osh = s.D;
-    q = w.rb_q;
-    k = w.rb_k;
-    v = w.rb_v;
-    o = w.rb_out;
+    s.permuted = 1;
   }
   if (!s.dense) {
     if ((rc = launched(sa::launch_pool_q(s, q, w, st), "pool_q"))) return rc;
@@ -410,10 +398,7 @@ int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void*
   if (!s.dense) {
     if ((rc = launched(sa::launch_select(s, w, st), "select"))) return rc;
   }
-  if ((rc = launched(sa::launch_attend(s, q, o, w, st), "attend"))) return rc;
-  if (s.reblock) {
-    if ((rc = launched(sa::launch_reblock_scatter(plan->shape, out, w, st), "reblock scatter"))) return rc;
-  }
+  if ((rc = launched(sa::launch_attend(s, q, out, w, st), "attend"))) return rc;
   return ok();
 }
 

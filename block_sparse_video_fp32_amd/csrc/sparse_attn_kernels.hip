@@ -71,6 +71,16 @@ __device__ __forceinline__ void store_stream(void* dst, uint32_t x, uint32_t y, 
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Row of the caller's Q (side 0) or K and V (side 1) behind row r of (b, h)
+// on the path: with Spark-Reblock orders in use, row rb_r0 + i is the
+// caller's row rb_r0 + order[i] of the partition's final order (the prefix
+// blocks stay); otherwise r itself.
+__device__ __forceinline__ int src_row(const Shape& s, const Workspace& ws, int side, long long bh, int r) {
+  if (!s.permuted || r < s.rb_r0) return r;
+  const long long p = (long long)side * s.B * s.H + bh;
+  return s.rb_r0 + ws.rb_ord[((long long)(s.rb_levels & 1) * s.rb_P + p) * s.rb_n + (r - s.rb_r0)];
+}
+
 // float -> bf16 bits, round to nearest even (NaN kept quiet).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   uint32_t u = __float_as_uint(x);
@@ -127,20 +137,21 @@ __global__ __launch_bounds__(256) void pool_q_kernel(Shape s, const uint16_t* __
   const int r0 = j * kBlock + half * RPS;
   const int rend = min(s.N, r0 + RPS);
   if (active && r0 < rend) {
-    const uint16_t* p = q + (long long)b * s.isb + (long long)h * s.ish + d0 + (long long)r0 * s.ist;
+    const uint16_t* p = q + (long long)b * s.isb + (long long)h * s.ish + d0;
     const int n = rend - r0;
     int r = 0;
     for (; r + 8 <= n; r += 8) {
       uint4 x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const uint4*>(p + (long long)(r + u) * s.ist);
+      for (int u = 0; u < 8; ++u)
+        x[u] = *reinterpret_cast<const uint4*>(p + (long long)src_row(s, ws, 0, bh, r0 + r + u) * s.ist);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += lane_bf16(x[u], e);
     }
     for (; r < n; ++r) {
-      const uint4 x = *reinterpret_cast<const uint4*>(p + (long long)r * s.ist);
+      const uint4 x = *reinterpret_cast<const uint4*>(p + (long long)src_row(s, ws, 0, bh, r0 + r) * s.ist);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += lane_bf16(x, e);
     }
@@ -260,15 +271,16 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Shape s, const uint16_t* _
   if (s.reweight && tid < D) al[tid] = ws.anchor[bh * D + tid];
 
   const int n = min(kBlock, s.N - j * kBlock);
-  const long long base = (long long)b * s.isb + (long long)h * s.ish + (long long)j * kBlock * s.ist;
+  const long long base = (long long)b * s.isb + (long long)h * s.ish;
 #pragma unroll
   for (int i = 0; i < CPR / 4; ++i) {
     const int id = tid + 256 * i;
     const int row = id / CPR, col = id % CPR;
     uint4 xk = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
     if (row < n) {
-      xk = *reinterpret_cast<const uint4*>(k + base + (long long)row * s.ist + col * 8);
-      xv = *reinterpret_cast<const uint4*>(v + base + (long long)row * s.ist + col * 8);
+      const long long off = base + (long long)src_row(s, ws, 1, bh, j * kBlock + row) * s.ist + col * 8;
+      xk = *reinterpret_cast<const uint4*>(k + off);
+      xv = *reinterpret_cast<const uint4*>(v + off);
     }
     *reinterpret_cast<uint4*>(Kl + row * LS + col * 8) = xk;
     *reinterpret_cast<uint4*>(Vl + row * LS + col * 8) = xv;
@@ -896,9 +908,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Q8 ? 2 : 3,
 
   // Q^T B-operand fragments: lane l holds Q[row l % 32][16 k + 8 (l/32) .. +8].
   const int qrow = (a0 + x) * kBlock + 32 * (w & 1) + l32;
+  const int qorig = (exists && qrow < N) ? src_row(s, ws, 0, bh, qrow) : 0;  // the caller's row
   bf16x8 qf[NK];
   {
-    const uint16_t* qp = q + (long long)b * s.isb + (long long)h * s.ish + (long long)qrow * s.ist + 8 * hh;
+    const uint16_t* qp = q + (long long)b * s.isb + (long long)h * s.ish + (long long)qorig * s.ist + 8 * hh;
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
       uint4 v4 = make_uint4(0, 0, 0, 0);
@@ -1293,7 +1306,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Q8 ? 2 : 3,
   const float l = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
   const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
   if (exists && qrow < N) {
-    uint16_t* o = out + (long long)b * s.osb + (long long)h * s.osh + (long long)qrow * s.ost + 4 * hh;
+    uint16_t* o = out + (long long)b * s.osb + (long long)h * s.osh + (long long)qorig * s.ost + 4 * hh;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll

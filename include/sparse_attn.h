@@ -99,7 +99,8 @@ extern "C" {
  * direction, pivot b = the row least similar to a, and the left child takes
  * the rows ranked first by u^T M (u_b - u_a), ties by position; children
  * keep their parent's order.  The path then runs on Q, K, V in the new
- * orders and the output rows are put back.  sparse_attn_forward only (the
+ * orders, reading their rows through the orders, and writes every output
+ * row at its own position.  sparse_attn_forward only (the
  * stage calls reject it); off on the dense path, whose result does not
  * depend on the order. */
 #define SA_FLAG_REBLOCK 32u
@@ -180,10 +181,11 @@ typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
  *                     reblock_levels % 2 holds the final order: new
  *                     position 64 * prefix_blocks + i holds row
  *                     64 * prefix_blocks + order[p][i].
- *   rb_keys           scratch; rb_qkv, rb_out: bf16 [B, N, H, D] copies of
- *                     Q, K, V in the new orders and the output before the
- *                     rows are put back (the sections above then describe
- *                     these copies).
+ *   rb_keys           scratch.
+ *   rb_qkv, rb_out    empty (no reordered copies are made).  After
+ *                     sparse_attn_forward the sections above describe the
+ *                     path in the new orders: block j of (b, h) holds the
+ *                     rows at new positions 64 j .. 64 j + 63.
  * After sparse_attn_select:
  *   counts            int32 [B, H, n_b]: selected key blocks per query block.
  *   lists             int32 [B, H, n_b, n_b]: the selected key blocks in
@@ -224,8 +226,9 @@ int sparse_attn_workspace_bytes(const sparse_attn_plan* plan, size_t* bytes);
 
 /* Full forward: pool, select and attend (pool and attend alone on the dense
  * path) enqueued on `stream` (a hipStream_t; NULL is the null stream); with
- * SA_FLAG_REBLOCK, first the partition and the reordered copies of q, k, v
- * in ws, then the same steps on them, then the output rows put back.
+ * SA_FLAG_REBLOCK, first the partition, then the same steps reading the
+ * rows of q, k, v through the new orders and writing each output row at its
+ * own position.
  * q, k, v are read-only bf16 device pointers and may alias one another; out
  * is a bf16 device pointer that must not overlap them or ws.  ws points to at
  * least layout.total_bytes of device memory (256-byte aligned), ws_bytes is

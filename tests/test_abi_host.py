@@ -209,8 +209,9 @@ def test_int8_flag_is_accepted(lib):
 
 
 def test_reblock_layout_and_stage_calls(lib):
-    """SA_FLAG_REBLOCK adds the partition sections (sizes as documented) and
-    runs through sparse_attn_forward only: the stage calls refuse the plan
+    """SA_FLAG_REBLOCK adds the partition sections (sizes as documented; the
+    copy sections rb_qkv and rb_out are empty) and runs through
+    sparse_attn_forward only: the stage calls refuse the plan
     before touching any device."""
     from block_sparse_video_fp32_amd.binding import SA_FLAG_REBLOCK
     assert SA_FLAG_REBLOCK == 32
@@ -220,11 +221,13 @@ def test_reblock_layout_and_stage_calls(lib):
     nv, P = N - 128, 2 * B * H
     assert L["reblock_levels"] == 4  # ceil(872 / 64) = 14 blocks
     sizes = dict(rb_gram=P * 1 * D * D * 4, rb_metric=P * D * D * 4, rb_units=P * nv * D * 2,
-                 rb_munits=P * nv * D * 2, rb_order=2 * P * nv * 4, rb_keys=P * nv * 4, rb_qkv=3 * B * N * H * D * 2, rb_out=B * N * H * D * 2)
+                 rb_munits=P * nv * D * 2, rb_order=2 * P * nv * 4, rb_keys=P * nv * 4, rb_qkv=0, rb_out=0)
     names = sorted(sizes, key=lambda n: L[n])
     ends = [L[n] for n in names[1:]] + [L["total_bytes"]]
     for n, e in zip(names, ends):
         assert e - L[n] >= sizes[n], n
+    # no reordered copies: the path reads its rows through the orders
+    assert L["rb_qkv"] == L["rb_out"] and L["rb_out"] >= L["rb_keys"] + sizes["rb_keys"]
     dense = binding.SparseAttnPlan(B, N, H, D, tau=-math.inf, reblock=True)
     assert dense.layout["reblock_levels"] == 0  # no effect on the dense path
     buf = ctypes.create_string_buffer(1 << 12)
