@@ -46,6 +46,22 @@ def _traffic(workload: str):
     return d.get("bytes_per_launch")
 
 
+def _mfma_busy(workload: str):
+    """Share of the attend kernel's cycles its MFMA pipes were busy
+    (SQ_VALU_MFMA_BUSY_CYCLES) from the committed rocprofv3 counter run, or
+    None when it is missing or was taken on other kernel source."""
+    p = os.path.join(ROOT, "profiles", f"attend_{workload}_mfma.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    from block_sparse_video_fp32_amd.profiling import kernel_source_hash
+
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return {k: round(d[k], 4) for k in ("mfma_busy_frac", "clock_ghz", "executed_mfma_tflop")}
+
+
 def selected_flops(plan, ws, N, D):
     """4 * D * rows_a * rows_c summed over every selected (b, h, a, c)."""
     import torch
@@ -62,6 +78,35 @@ def selected_flops(plan, ws, N, D):
     flops = 4.0 * D * (per_row * rows_a.view(1, 1, nb)).sum().item()
     density = counts.to(torch.float64).sum().item() / (counts.numel() * nb)
     return flops, density
+
+
+def attend_mfma_count(plan, ws, D, centroid=True):
+    """MFMA instructions one launch of the default attend instance executes.
+
+    A query block's two waves each run one 32-key half tile with D/16 k-steps
+    for S^T and (D/32 column tiles) x 2 k-steps for PV, i.e. D/8
+    v_mfma_f32_32x32x16_bf16.  A block runs both half tiles of every key block
+    in its list, and, when it is routed (count < n_b) with centroids on, one
+    centroid half tile for each group of 32 key blocks that holds at least one
+    unselected block.  Rows are counted from the routing lists, so the figure
+    is exact for the launch (no logit overflow recompute assumed)."""
+    import torch
+
+    counts, lists = plan.route_views(ws)
+    B, H, nb = counts.shape
+    idx = torch.arange(nb, device=counts.device, dtype=torch.int32)
+    valid = idx.view(1, 1, 1, nb) < counts.unsqueeze(-1)
+    col = torch.where(valid, lists.clamp(0, nb - 1), nb).long()
+    nct = (nb + 31) // 32
+    sel = torch.zeros(B, H, nb, 32 * nct + 1, dtype=torch.bool, device=counts.device)
+    sel[..., nb:] = True  # padding past the last block never needs a centroid
+    sel.scatter_(-1, col, True)
+    half_tiles = 2 * int(counts.to(torch.int64).sum().item())
+    if centroid:
+        chunk_unsel = (~sel[..., : 32 * nct]).view(B, H, nb, nct, 32).any(-1)
+        need = chunk_unsel & (counts < nb).unsqueeze(-1)
+        half_tiles += int(need.sum().item())
+    return 2 * half_tiles * (D // 8)
 
 
 def cpu_baseline(w, seconds_target=20.0):
@@ -308,6 +353,7 @@ def main():
         },
         "density": round(density, 5),
         "selected_tflop_per_call": round(flops / 1e12, 4),
+        "attend_mfma_per_launch": attend_mfma_count(plan, ws, D),
         "dense_ms_per_call": None if dense_ms is None else round(dense_ms, 3),
         "speedup_vs_own_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
         "dense_equivalent_tflops": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
@@ -324,6 +370,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
+            "mfma_counters": _mfma_busy(args.workload),
         },
         "context": "pages' RTX 5090 figures at N=32768, H=56 (density 0.08): SDPA 144.5 ms, Sol-Attn 16.06 ms; other hardware and inputs, not a target",
     }

@@ -10,6 +10,14 @@
     python -m block_sparse_video_fp32_amd.profiling traffic FETCH_DIR WRITE_DIR \\
         --kernel attend_kernel --copy-bytes 268435456 --out FILE.json
 
+    # MFMA work and MFMA-pipe utilisation of one kernel from one --pmc run of
+    # SQ_INSTS_VALU_MFMA_BF16 SQ_INSTS_VALU_MFMA_MOPS_BF16
+    # SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32
+    # SQ_INSTS_LDS SQ_BUSY_CYCLES GRBM_GUI_ACTIVE, set against the JSON line
+    # bench.py printed in the same run (selected FLOPs, expected MFMA count)
+    python -m block_sparse_video_fp32_amd.profiling mfma PMC_DIR BENCH.json \\
+        --kernel "attend_kernel<128, 2, false, false>" --out FILE.json
+
 The directories are rocprofv3 ``-d`` output directories written with
 ``--output-format csv``.
 """
@@ -102,6 +110,78 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int):
     return res
 
 
+MFMA_COUNTERS = (
+    "SQ_INSTS_VALU_MFMA_BF16",
+    "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+    "SQ_VALU_MFMA_BUSY_CYCLES",
+    "SQ_INSTS_VALU",
+    "SQ_INSTS_VALU_TRANS_F32",
+    "SQ_INSTS_LDS",
+    "SQ_BUSY_CYCLES",
+    "GRBM_GUI_ACTIVE",
+)
+N_XCD = 8       # MI355X: GRBM_GUI_ACTIVE is summed over its 8 XCDs
+N_SIMD = 1024   # 256 CUs x 4 SIMDs; SQ_VALU_MFMA_BUSY_CYCLES is summed over them
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def dispatch_durations(dirname: str, kernel_substr: str):
+    """{dispatch_id: ns} from the timestamps of a counter collection."""
+    path = _find(dirname, "counter_collection.csv")
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel_substr in r["Kernel_Name"]:
+                out[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return out
+
+
+def mfma(pmc_dir: str, bench_line: dict, kernel: str):
+    """Executed MFMA work and MFMA-pipe busy share of a kernel, per launch.
+
+    The MOPS counter counts bf16 MFMA work in units of 512 FLOPs.  The busy
+    share divides the summed per-SIMD MFMA busy cycles by the SIMD count times
+    the active cycles of one XCD."""
+    per = {}
+    for c in MFMA_COUNTERS:
+        vals, _ = counter_per_dispatch(pmc_dir, c, kernel)
+        if not vals:
+            raise RuntimeError(f"{c}: no dispatch of {kernel}")
+        per[c] = sum(vals.values()) / len(vals)
+        ndisp = len(vals)
+    dur = dispatch_durations(pmc_dir, kernel)
+    dur_ns = sum(dur.values()) / len(dur)
+    gui_xcd = per["GRBM_GUI_ACTIVE"] / N_XCD
+    flops_exec = per["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+    sel = bench_line["selected_tflop_per_call"] * 1e12
+    expected = bench_line.get("attend_mfma_per_launch")
+    res = {
+        "kernel": kernel,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "dispatches": ndisp,
+        "counters_per_dispatch": per,
+        "duration_us": dur_ns / 1e3,
+        "clock_ghz": gui_xcd / dur_ns,
+        "mfma_instructions": per["SQ_INSTS_VALU_MFMA_BF16"],
+        "mfma_instructions_expected": expected,
+        "executed_mfma_tflop": flops_exec / 1e12,
+        "selected_tflop": sel / 1e12,
+        "flop_per_mfma": flops_exec / per["SQ_INSTS_VALU_MFMA_BF16"],
+        "mfma_busy_frac": per["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * gui_xcd),
+        "mfma_busy_cycles_per_mfma": per["SQ_VALU_MFMA_BUSY_CYCLES"] / per["SQ_INSTS_VALU_MFMA_BF16"],
+        "executed_tflops": flops_exec / (dur_ns * 1e-9) / 1e12,
+        "selected_tflops": sel / (dur_ns * 1e-9) / 1e12,
+        "executed_frac_of_peak": flops_exec / (dur_ns * 1e-9) / 1e12 / PEAK_BF16_TFLOPS,
+        "selected_frac_of_peak": sel / (dur_ns * 1e-9) / 1e12 / PEAK_BF16_TFLOPS,
+        "trans_per_mfma": per["SQ_INSTS_VALU_TRANS_F32"] / per["SQ_INSTS_VALU_MFMA_BF16"],
+        "valu_per_mfma": per["SQ_INSTS_VALU"] / per["SQ_INSTS_VALU_MFMA_BF16"],
+        "lds_per_mfma": per["SQ_INSTS_LDS"] / per["SQ_INSTS_VALU_MFMA_BF16"],
+    }
+    if expected:
+        res["mfma_instructions_ratio"] = per["SQ_INSTS_VALU_MFMA_BF16"] / expected
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -113,13 +193,23 @@ def main(argv=None):
     b.add_argument("--kernel", default="attend_kernel")
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--out")
+    m = sub.add_parser("mfma")
+    m.add_argument("pmc_dir")
+    m.add_argument("bench_json", help="file holding the JSON line bench.py printed in the counter run")
+    m.add_argument("--kernel", default="attend_kernel<128, 2, false, false>")
+    m.add_argument("--out")
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10}  kernel")
         for name, n, tot, avg, mn, mx in kernel_stats(args.dir):
             print(f"{n:6d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f} {tot / 1e6:10.3f}  {name[:110]}")
     else:
-        res = traffic(args.fetch_dir, args.write_dir, args.kernel, args.copy_bytes)
+        if args.cmd == "mfma":
+            with open(args.bench_json) as f:
+                line = [x for x in f.read().splitlines() if x.startswith("{")][-1]
+            res = mfma(args.pmc_dir, json.loads(line), args.kernel)
+        else:
+            res = traffic(args.fetch_dir, args.write_dir, args.kernel, args.copy_bytes)
         text = json.dumps(res, indent=2)
         if args.out:
             with open(args.out, "w") as f:
