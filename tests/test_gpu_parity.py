@@ -299,6 +299,11 @@ SMALL = [
     ("dense_d64", dict(B=2, N=256, H=1, D=64), dict(tau=-math.inf)),
     ("one_row", dict(B=1, N=1, H=1, D=64), dict(tau=1.0)),
     ("one_block", dict(B=1, N=64, H=2, D=128), dict(tau=1.0)),
+    # every row a prefix row: all query blocks dense through the routed path
+    ("prefix_all", dict(B=1, N=300, H=2, D=64), dict(tau=1.0, prefix_len=300)),
+    # every block selected by routing (no centroid tiles), not by the dense flag
+    ("topk_all", dict(B=1, N=700, H=2, D=128), dict(topk_ratio=1.0)),
+    ("tau_neg_huge", dict(B=1, N=777, H=2, D=64), dict(tau=-1e30)),
 ]
 
 
