@@ -18,6 +18,11 @@
     python -m block_sparse_video_fp32_amd.profiling mfma PMC_DIR BENCH.json \\
         --kernel "attend_kernel<128, 2, false, false>" --out FILE.json
 
+    # any counters of one kernel from one --pmc run, per dispatch, and per
+    # CU-cycle of one XCD's GRBM_GUI_ACTIVE when that counter is in the run
+    python -m block_sparse_video_fp32_amd.profiling counters PMC_DIR \\
+        --kernel "attend_kernel<128, 2, false, false>" --out FILE.json
+
 The directories are rocprofv3 ``-d`` output directories written with
 ``--output-format csv``.
 """
@@ -182,6 +187,39 @@ def mfma(pmc_dir: str, bench_line: dict, kernel: str):
     return res
 
 
+N_CU = 256  # MI355X compute units
+
+
+def counters(pmc_dir: str, kernel: str):
+    """Per-dispatch averages of every counter collected for a kernel.  SQ
+    counters are also given per CU-cycle (summed value / (256 CUs x the
+    active cycles of one XCD)); SQ_WAVE_CYCLES counts quad-cycles, so
+    4 x its per-CU-cycle figure is the mean number of resident waves per CU."""
+    path = _find(pmc_dir, "counter_collection.csv")
+    names = set()
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"]:
+                names.add(r["Counter_Name"])
+    if not names:
+        raise RuntimeError(f"no dispatch of {kernel}")
+    per = {}
+    for c in sorted(names):
+        vals, _ = counter_per_dispatch(pmc_dir, c, kernel)
+        per[c] = sum(vals.values()) / len(vals)
+        ndisp = len(vals)
+    dur = dispatch_durations(pmc_dir, kernel)
+    res = {"kernel": kernel, "kernel_source_sha256_16": kernel_source_hash(), "dispatches": ndisp,
+           "counters_per_dispatch": per, "duration_us": sum(dur.values()) / len(dur) / 1e3}
+    if "GRBM_GUI_ACTIVE" in per:
+        gx = per["GRBM_GUI_ACTIVE"] / N_XCD
+        res["clock_ghz"] = gx / (res["duration_us"] * 1e3)
+        res["per_cu_cycle"] = {c: v / (N_CU * gx) for c, v in per.items() if c.startswith("SQ_")}
+        if "SQ_WAVE_CYCLES" in per:
+            res["resident_waves_per_cu"] = 4.0 * per["SQ_WAVE_CYCLES"] / (N_CU * gx)
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -198,13 +236,19 @@ def main(argv=None):
     m.add_argument("bench_json", help="file holding the JSON line bench.py printed in the counter run")
     m.add_argument("--kernel", default="attend_kernel<128, 2, false, false>")
     m.add_argument("--out")
+    c = sub.add_parser("counters")
+    c.add_argument("pmc_dir")
+    c.add_argument("--kernel", default="attend_kernel<128, 2, false, false>")
+    c.add_argument("--out")
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10}  kernel")
         for name, n, tot, avg, mn, mx in kernel_stats(args.dir):
             print(f"{n:6d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f} {tot / 1e6:10.3f}  {name[:110]}")
     else:
-        if args.cmd == "mfma":
+        if args.cmd == "counters":
+            res = counters(args.pmc_dir, args.kernel)
+        elif args.cmd == "mfma":
             with open(args.bench_json) as f:
                 line = [x for x in f.read().splitlines() if x.startswith("{")][-1]
             res = mfma(args.pmc_dir, json.loads(line), args.kernel)
