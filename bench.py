@@ -300,8 +300,9 @@ def main():
             print(f"# {name}: {m_call:.3f} ms/call (pool {m_pool:.3f}, attend {m_att:.3f})", file=sys.stderr,
                   flush=True)
             del mws, mplan
-        # Spark-Reblock runs through the forward call (partition + reorder +
-        # the path on the reordered copies + rows put back)
+        # Spark-Reblock runs through the forward call (the partition, then the
+        # path reading Q, K, V rows through the final order and writing each
+        # output row at its own position)
         mplan = binding.SparseAttnPlan(B, N, H, D, prefix_len=w.prefix_len, reblock=True, **rkw)
         mws = mplan.workspace(dev)
         for _ in range(2):

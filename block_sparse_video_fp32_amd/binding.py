@@ -267,20 +267,47 @@ class SparseAttnPlan:
         return ws
 
     # -- argument checks (marshalling only) --------------------------------
-    def _check_io(self, *ts):
+    def strides(self, which: str) -> Tuple[int, int, int]:
+        """Element strides (b, t, h) the plan reads q, k, v with (``"in"``) or
+        writes out with (``"out"``): the contiguous BTHD strides when the
+        plan was given none."""
+        p = self.params
+        sb, st, sh = ((p.in_stride_b, p.in_stride_t, p.in_stride_h) if which == "in"
+                      else (p.out_stride_b, p.out_stride_t, p.out_stride_h))
+        if sb == 0 and st == 0 and sh == 0:
+            B, N, H, D = self.shape
+            return (N * H * D, H * D, D)
+        return (int(sb), int(st), int(sh))
+
+    def _check_io(self, ins=(), outs=()):
+        """dtype, shape, device and strides of the tensors against the plan.
+
+        The library addresses element (b, t, h, d) of q, k and v as
+        b * in_stride_b + t * in_stride_t + h * in_stride_h + d (out with its
+        own strides), so a tensor whose strides differ from the plan's would
+        be read or written at the wrong places: that is an error here.  The
+        stride of a dimension of size 1 is never used and is not compared."""
         import torch
 
-        for t in ts:
-            if t is None:
-                continue
-            if t.dtype != torch.bfloat16:
-                raise TypeError("q, k, v and out must be torch.bfloat16")
-            if tuple(t.shape) != self.shape:
-                raise ValueError(f"tensor shape {tuple(t.shape)} != plan shape {self.shape}")
-            if t.stride(3) != 1:
-                raise ValueError("the head dimension must be contiguous")
-            if t.device.type != "cuda":
-                raise ValueError("tensors must live on a HIP device")
+        for group, which in ((ins, "in"), (outs, "out")):
+            want = self.strides(which)
+            for t in group:
+                if t is None:
+                    continue
+                if t.dtype != torch.bfloat16:
+                    raise TypeError("q, k, v and out must be torch.bfloat16")
+                if tuple(t.shape) != self.shape:
+                    raise ValueError(f"tensor shape {tuple(t.shape)} != plan shape {self.shape}")
+                if t.stride(3) != 1:
+                    raise ValueError("the head dimension must be contiguous")
+                got = tuple(t.stride()[:3])
+                for dim, (g, w_) in enumerate(zip(got, want)):
+                    if t.shape[dim] > 1 and g != w_:
+                        raise ValueError(
+                            f"{'input' if which == 'in' else 'output'} strides {got} differ from the plan's "
+                            f"{want} (build the plan with {which}_strides matching the tensors)")
+                if t.device.type != "cuda":
+                    raise ValueError("tensors must live on a HIP device")
 
     def _call(self, fn, name, device, *args):
         import torch
@@ -293,14 +320,14 @@ class SparseAttnPlan:
 
         if out is None:
             out = torch.empty_like(q)
-        self._check_io(q, k, v, out)
+        self._check_io(ins=(q, k, v), outs=(out,))
         ws = self.workspace(q.device) if ws is None else ws
         self._call(self._lib.sparse_attn_forward, "sparse_attn_forward", q.device,
                    _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws), ws.numel())
         return out
 
     def pool(self, q, k, v, ws=None):
-        self._check_io(q, k, v)
+        self._check_io(ins=(q, k, v))
         ws = self.workspace(q.device) if ws is None else ws
         self._call(self._lib.sparse_attn_pool, "sparse_attn_pool", q.device,
                    _ptr(q), _ptr(k), _ptr(v), _ptr(ws), ws.numel())
@@ -308,7 +335,7 @@ class SparseAttnPlan:
 
     def route(self, q, k, v, ws=None):
         """Steps 1-3 (pool and select): counts and lists in ws."""
-        self._check_io(q, k, v)
+        self._check_io(ins=(q, k, v))
         ws = self.workspace(q.device) if ws is None else ws
         self._call(self._lib.sparse_attn_route, "sparse_attn_route", q.device,
                    _ptr(q), _ptr(k), _ptr(v), _ptr(ws), ws.numel())
@@ -320,7 +347,7 @@ class SparseAttnPlan:
 
     def attend(self, q, out, ws):
         """Step 4 alone; reads the packed tiles and lists already in ws."""
-        self._check_io(q, out)
+        self._check_io(ins=(q,), outs=(out,))
         self._call(self._lib.sparse_attn_attend, "sparse_attn_attend", q.device,
                    _ptr(q), _ptr(out), _ptr(ws), ws.numel())
         return out

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -49,7 +50,19 @@ std::mutex g_dev_mu;
 std::vector<int> g_dev_ok;            // 0 unknown, 1 gfx950, -1 other
 std::vector<std::string> g_dev_arch;  // arch name as reported
 
+// Test hook for the mismatch error: SPARSE_ATTN_ARCH_OVERRIDE=<name> makes
+// the check report <name> as the detected architecture without querying any
+// device.  It can only refuse: a value naming gfx950 is ignored and the real
+// device is checked as usual.
+const char* arch_override() {
+  const char* o = std::getenv("SPARSE_ATTN_ARCH_OVERRIDE");
+  if (!o || !*o || std::strncmp(o, "gfx950", 6) == 0) return nullptr;
+  return o;
+}
+
 int check_device() {
+  if (const char* o = arch_override())
+    return fail(SA_EUNSUPPORTED_DEVICE, "requires gfx950, found %s (SPARSE_ATTN_ARCH_OVERRIDE)", o);
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess || dev < 0)
@@ -269,6 +282,39 @@ int check_tensors(const void* q, const void* k, const void* v, const void* out, 
   return SA_OK;
 }
 
+// SPARSE_ATTN_LOG=1: one compact line per plan on stderr (shape, routing,
+// flags, blocks, workspace), so that a run shows what each call does without
+// per-call output.
+bool log_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("SPARSE_ATTN_LOG");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void log_plan(const sparse_attn_plan* pl) {
+  if (!log_on()) return;
+  const sparse_attn_params& p = pl->params;
+  const sa::Shape& s = pl->shape;
+  char route[64];
+  if (s.dense)
+    std::snprintf(route, sizeof(route), "dense (tau=-inf)");
+  else if (p.route == SA_ROUTE_TOPK)
+    std::snprintf(route, sizeof(route), "topk %.4g (k=%d)", (double)p.topk_ratio, s.topk);
+  else
+    std::snprintf(route, sizeof(route), "tau %.4g", (double)p.tau);
+  std::fprintf(stderr,
+               "sparse_attn: plan B=%d N=%d H=%d D=%d n_b=%d tail=%d | %s | prefix %d rows (%d blocks, %s) | "
+               "centroid %d logmass %d reweight %d int8_qk %d reblock %d (%d levels) | scale %.6g | "
+               "workspace %.1f MiB\n",
+               p.B, p.N, p.H, p.D, s.nb, s.tail, route, p.prefix_len, s.pb,
+               s.prefix_rows ? "exact_kv_and_rows" : "exact_kv", s.centroid, (p.flags & SA_FLAG_LOGMASS) ? 1 : 0,
+               s.reweight, s.int8, s.reblock, s.reblock ? s.rb_levels : 0, (double)s.scale,
+               (double)pl->layout.total_bytes / (1024.0 * 1024.0));
+  std::fflush(stderr);
+}
+
 int launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SA_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
   return SA_OK;
@@ -306,6 +352,7 @@ int sparse_attn_plan_create(const sparse_attn_params* params, sparse_attn_plan**
   pl->params = *params;
   build_plan(pl);
   *plan = pl;
+  log_plan(pl);
   return ok();
 }
 

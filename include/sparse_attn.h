@@ -210,21 +210,41 @@ typedef struct sparse_attn_ws_layout {
 } sparse_attn_ws_layout;
 
 /* Validates *params (host only, touches no device) and creates a plan.
+ * The Star7 README, section 环境与分发, describes the native library
+ * boundary this follows: the library is handed tensor addresses, shapes and
+ * the current stream only and links no PyTorch ABI; the plan is the host
+ * record of shape, strides and routing those calls share.  (The call is
+ * named sparse_attn_plan_create because sparse_attn_plan is the name of the
+ * opaque plan type in C.)
+ * params: read only, copied into the plan.  *plan: receives a plan owned by
+ * the caller until sparse_attn_plan_destroy.
  * Returns SA_EINVAL / SA_EUNSUPPORTED_SHAPE / SA_EALIGN on bad input, in
- * which case *plan is set to NULL. */
+ * which case *plan is set to NULL.  With the environment variable
+ * SPARSE_ATTN_LOG=1 each plan prints one summary line on stderr (shape,
+ * routing, prefix mode, flags, workspace size), in the spirit of the compact
+ * verbose summary of the Star7 README, section 错误处理与日志. */
 int sparse_attn_plan_create(const sparse_attn_params* params, sparse_attn_plan** plan);
 
-/* Frees a plan (NULL is ignored). */
+/* Frees a plan (NULL is ignored).  Host only; no device memory is involved
+ * (Star7 README, 环境与分发: the caller owns the tensors). */
 void sparse_attn_plan_destroy(sparse_attn_plan* plan);
 
-/* Fills *layout for the plan's shape (host only). */
+/* Fills *layout for the plan's shape (host only): the byte offsets of the
+ * workspace sections described above.  Returns SA_EINVAL on NULL
+ * arguments. */
 int sparse_attn_workspace_layout(const sparse_attn_plan* plan, sparse_attn_ws_layout* layout);
 
 /* *bytes = the device workspace a call with this plan needs
- * (layout.total_bytes; host only). */
+ * (layout.total_bytes; host only).  The caller allocates it (the library
+ * never allocates device memory: Star7 README, 环境与分发, addresses only).
+ * Returns SA_EINVAL on NULL arguments. */
 int sparse_attn_workspace_bytes(const sparse_attn_plan* plan, size_t* bytes);
 
-/* Full forward: pool, select and attend (pool and attend alone on the dense
+/* Full forward, the method of the Star7 README, section 工作原理 > Sol
+ * (blockwise routing, exact selected blocks, centroids of the missed ones in
+ * one FP32 softmax), across the boundary of its section 环境与分发
+ * (addresses, shapes and the current stream; strict architecture check, no
+ * fallback): pool, select and attend (pool and attend alone on the dense
  * path) enqueued on `stream` (a hipStream_t; NULL is the null stream); with
  * SA_FLAG_REBLOCK, first the partition, then the same steps reading the
  * rows of q, k, v through the new orders and writing each output row at its
@@ -236,26 +256,36 @@ int sparse_attn_workspace_bytes(const sparse_attn_plan* plan, size_t* bytes);
 int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
                         void* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Step 1 alone: block means of Q, K, V and the packed K, V^T and centroid
- * tiles (every section listed under "After sparse_attn_pool").  The stage
+/* Step 1 alone: block means of Q, K, V (Star7 README, 工作原理 > Sol: 64-row
+ * Q and K blocks; Spark-H3 news, Spark-Reweight bullet: mean-pooled K/V
+ * summaries) and the packed K, V^T and centroid tiles (every section listed
+ * under "After sparse_attn_pool").  Arguments and errors as
+ * sparse_attn_forward without out.  The stage
  * calls (pool, select, route, attend) refuse a SA_FLAG_REBLOCK plan with
  * SA_EINVAL: its steps run through sparse_attn_forward only. */
 int sparse_attn_pool(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
                      void* ws, size_t ws_bytes, void* stream);
 
 /* Steps 2-3 alone: scores every block pair from the pooled means already
- * in ws and writes counts and lists (threshold or top-K, sink, dense
- * prefix rows). */
+ * in ws and writes counts and lists: threshold mean + tau * std of the
+ * row's block scores (thakicloud accel-stack post, 이 기술은 무엇인가) or
+ * top-K ratio (Spark-H3 news, 워크플로), the prefix key sink and dense prefix
+ * query rows (Star7 README, Sol; aikraft.ru news, Нововведения версии 2.0).
+ * Returns SA_EINVAL (NULL plan or ws), SA_EWORKSPACE, SA_EALIGN,
+ * SA_EUNSUPPORTED_DEVICE or SA_ELAUNCH. */
 int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, void* stream);
 
 /* Steps 1-3: the routing of every query block (sparse_attn_pool followed
- * by sparse_attn_select), leaving counts and lists in ws for inspection or
- * for sparse_attn_attend.  Same arguments and errors as sparse_attn_pool;
+ * by sparse_attn_select; passages as cited there), leaving counts and lists
+ * in ws for inspection or for sparse_attn_attend.  Same arguments and errors as sparse_attn_pool;
  * on the dense path it only pools (there is nothing to route). */
 int sparse_attn_route(const sparse_attn_plan* plan, const void* q, const void* k, const void* v, void* ws,
                       size_t ws_bytes, void* stream);
 
-/* Step 4 alone: exact attention over each query block's list and centroid
+/* Step 4 alone (Star7 README, 工作原理 > Sol: selected blocks exact, every
+ * missed block through its centroid in the same FP32 softmax; Spark-H3 news,
+ * Spark-Reweight bullet: the log-mass bias): exact attention over each query
+ * block's list and centroid
  * terms for every other block, reading q and, from ws, the packed tiles,
  * counts and lists.  A caller may write its own lists: entries should be
  * distinct block indices in [0, n_b) (out-of-range entries are ignored and
@@ -265,14 +295,23 @@ int sparse_attn_route(const sparse_attn_plan* plan, const void* q, const void* k
 int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, void* out, void* ws, size_t ws_bytes,
                        void* stream);
 
-/* Static message for an error code. */
+/* Static message for an error code.  Errors are reported, never repaired:
+ * the Star7 README, section 环境与分发, stops the task on an architecture
+ * mismatch with an error naming the required and detected capability and
+ * no fallback backend, and its section 错误处理与日志 runs strict modes with
+ * no fallback. */
 const char* sparse_attn_strerror(int code);
 
 /* Thread-local detail of the last failing call on this thread ("" if none),
- * e.g. "requires gfx950, found gfx942". */
+ * e.g. "requires gfx950, found gfx942": the required and the detected
+ * architecture, as the Star7 README, section 环境与分发, asks of a mismatch.
+ * Test hook: with SPARSE_ATTN_ARCH_OVERRIDE set to an architecture name
+ * other than gfx950, every call that checks the device fails with
+ * SA_EUNSUPPORTED_DEVICE naming that architecture, without touching any
+ * device (the variable can only refuse, never admit a device). */
 const char* sparse_attn_last_error(void);
 
-/* SA_ABI_VERSION of the built library. */
+/* SA_ABI_VERSION of the built library (compare with the header's). */
 int sparse_attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -166,6 +166,56 @@ def test_call_validation_before_launch(lib):
     assert lib.sparse_attn_attend(h, fake, fake, fake, need - 1, None) == SA_EWORKSPACE
 
 
+def test_device_mismatch_names_required_and_detected_arch(lib, monkeypatch):
+    """An architecture mismatch is refused before any launch with
+    SA_EUNSUPPORTED_DEVICE and a message naming the required and the
+    detected architecture (Star7 README, 环境与分发), forced here by the
+    library's test hook, which never queries a device."""
+    SA_EUNSUPPORTED_DEVICE = -3
+    plan = binding.SparseAttnPlan(1, 1024, 2, 64)
+    h, need, fake = plan._h, plan.workspace_bytes, 1 << 20  # never dereferenced
+    lib.sparse_attn_attend.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]
+    monkeypatch.setenv("SPARSE_ATTN_ARCH_OVERRIDE", "gfx942")
+    calls = [
+        ("forward", lambda: lib.sparse_attn_forward(h, fake, fake, fake, fake, fake, need, None)),
+        ("pool", lambda: lib.sparse_attn_pool(h, fake, fake, fake, fake, need, None)),
+        ("select", lambda: lib.sparse_attn_select(h, fake, need, None)),
+        ("route", lambda: lib.sparse_attn_route(h, fake, fake, fake, fake, need, None)),
+        ("attend", lambda: lib.sparse_attn_attend(h, fake, fake, fake, need, None)),
+    ]
+    for name, call in calls:
+        assert call() == SA_EUNSUPPORTED_DEVICE, name
+        msg = lib.sparse_attn_last_error().decode()
+        assert "requires gfx950" in msg and "gfx942" in msg, msg
+    assert "gfx950" in lib.sparse_attn_strerror(SA_EUNSUPPORTED_DEVICE).decode()
+    # argument errors still come first (nothing reaches the device check)
+    assert lib.sparse_attn_forward(h, fake, fake, fake, fake, fake, need - 1, None) == SA_EWORKSPACE
+    # the binding surfaces it as an exception carrying the code and message
+    with pytest.raises(binding.SparseAttnError) as e:
+        binding._check(lib.sparse_attn_select(h, fake, need, None), "sparse_attn_select")
+    assert e.value.code == SA_EUNSUPPORTED_DEVICE and "gfx942" in str(e.value)
+
+
+def test_plan_log_line(tmp_path):
+    """SPARSE_ATTN_LOG=1 prints one summary line per plan on stderr."""
+    import subprocess
+    import sys
+
+    code = ("import sys; sys.path.insert(0, %r); from block_sparse_video_fp32_amd import binding; "
+            "binding.SparseAttnPlan(1, 38247, 4, 128, topk_ratio=0.1, prefix_len=1024, reweight=True)" % ROOT)
+    env = dict(os.environ, SPARSE_ATTN_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [x for x in r.stderr.splitlines() if x.startswith("sparse_attn: plan")]
+    assert len(lines) == 1, r.stderr
+    for part in ("N=38247", "n_b=598", "tail=39", "topk 0.1 (k=60)", "prefix 1024 rows (16 blocks",
+                 "reweight 1", "workspace"):
+        assert part in lines[0], (part, lines[0])
+    env.pop("SPARSE_ATTN_LOG")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert "sparse_attn: plan" not in r.stderr
+
+
 def test_binding_rejects_bad_tensors():
     import torch
 
@@ -176,6 +226,46 @@ def test_binding_rejects_bad_tensors():
     y = torch.zeros(1, 128, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         plan.forward(y, y, y)  # CPU tensors
+
+
+def test_binding_checks_strides_against_the_plan():
+    """A tensor whose strides differ from the plan's is refused before any
+    call (the library would address it with the plan's strides): a fused-QKV
+    view given to a contiguous plan, a non-contiguous output, a
+    batch-expanded (stride 0) input.  Strides of size-1 dimensions are never
+    used and are not compared."""
+    import torch
+
+    B, N, H, D = 2, 128, 3, 64
+    plan = binding.SparseAttnPlan(B, N, H, D)
+    assert plan.strides("in") == plan.strides("out") == (N * H * D, H * D, D)
+    fused = torch.zeros(B, N, 3, H, D, dtype=torch.bfloat16)
+    q = fused[:, :, 0]
+    with pytest.raises(ValueError, match="input strides"):
+        plan._check_io(ins=(q,))
+    big = torch.zeros(B, N, 2, H, D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="output strides"):
+        plan._check_io(outs=(big[:, :, 1],))
+    one = torch.zeros(1, N, H, D, dtype=torch.bfloat16).expand(B, N, H, D)
+    assert one.stride(0) == 0
+    with pytest.raises(ValueError, match="input strides"):
+        plan._check_io(ins=(one,))
+    # matching strides pass the stride check and stop at the device check
+    c = torch.zeros(B, N, H, D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        plan._check_io(ins=(c, c, c), outs=(c,))
+    fplan = binding.SparseAttnPlan(B, N, H, D, in_strides=q.stride()[:3], out_strides=big[:, :, 1].stride()[:3])
+    with pytest.raises(ValueError, match="HIP device"):
+        fplan._check_io(ins=(q, fused[:, :, 1], fused[:, :, 2]), outs=(big[:, :, 1],))
+    with pytest.raises(ValueError, match="input strides"):
+        fplan._check_io(ins=(c,))
+    # B = 1: the batch stride is never used
+    p1 = binding.SparseAttnPlan(1, N, H, D)
+    odd = torch.zeros(1, N, 2, H, D, dtype=torch.bfloat16)[:, :, 0]
+    with pytest.raises(ValueError, match="input strides"):  # t and h strides still differ
+        p1._check_io(ins=(odd,))
+    with pytest.raises(ValueError, match="HIP device"):
+        p1._check_io(ins=(torch.zeros(2, N, H, D, dtype=torch.bfloat16)[1:],))
 
 
 def test_plan_error_raises():
