@@ -30,6 +30,10 @@ Workload recipes (random-number draw order is part of the recipe):
   ``s_hd(f,y,x) = (1/sqrt 2) sum_j sin(2 pi (f/Pf + y/Py + x/Px)_hdj + phi_hdj)``
   with every period log-uniform in [2, 32] (draw order Pf, Py, Px, phi), then
   the Q noise, then V.  Q = K = bf16(1.5 s + N(0,1)), V = bf16(N(0,1)).
+* ``clustered_soft`` and ``h3_joint(..., amp=0.5, shared_qk=False)``: test
+  inputs with the same signals, a weaker amplitude and independent key noise
+  (drawn after the query noise), so that no key copies its query and the
+  centroid terms carry much of each row's softmax mass.
 """
 
 from __future__ import annotations
@@ -46,6 +50,7 @@ __all__ = [
     "make_workload",
     "iid",
     "clustered",
+    "clustered_soft",
     "h3_joint",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
@@ -157,13 +162,13 @@ def _smooth_1d(rng, B, N, H, D):
     return _sum_of_sines(ang, N, H, D)
 
 
-def _signal_plus_noise(rng, s, B):
-    """bf16(1.5 s + N(0,1)) with s [rows, H, D] shared by every batch entry."""
+def _signal_plus_noise(rng, s, B, amp=1.5):
+    """bf16(amp s + N(0,1)) with s [rows, H, D] shared by every batch entry."""
     import torch
 
     rows, H, D = s.shape
     noise = torch.from_numpy(rng.standard_normal((B, rows, H, D), dtype=np.float32))
-    return _bf16(noise.add_(torch.from_numpy(s)[None], alpha=1.5))
+    return _bf16(noise.add_(torch.from_numpy(s)[None], alpha=amp))
 
 
 def clustered(B: int, N: int, H: int, D: int, seed: int):
@@ -175,8 +180,27 @@ def clustered(B: int, N: int, H: int, D: int, seed: int):
     return q, q, v
 
 
-def h3_joint(B: int, N: int, H: int, D: int, prefix_len: int, seed: int):
-    """Packed joint sequence: an i.i.d. prefix, then a frames x 24 x 42 video grid."""
+def clustered_soft(B: int, N: int, H: int, D: int, seed: int, amp: float = 0.5):
+    """The clustered signal with independent query and key noise and a
+    weaker signal: Q = bf16(amp s + N(0,1)), K = bf16(amp s + N'(0,1)),
+    V = bf16(N(0,1)).  Draws: periods, phases, Q noise, K noise, V.  Routing
+    still follows the smooth signal, but no key copies its query, so each
+    row's softmax mass spreads over many blocks and the unselected blocks'
+    centroid terms carry a large share of it (test inputs for the centroid
+    path; the benchmarked workloads use ``clustered``)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    s = _smooth_1d(rng, B, N, H, D)
+    q = _signal_plus_noise(rng, s, B, amp)
+    k = _signal_plus_noise(rng, s, B, amp)
+    v = _bf16(rng.standard_normal((B, N, H, D), dtype=np.float32))
+    return q, k, v
+
+
+def h3_joint(B: int, N: int, H: int, D: int, prefix_len: int, seed: int, amp: float = 1.5,
+             shared_qk: bool = True):
+    """Packed joint sequence: an i.i.d. prefix, then a frames x 24 x 42 video
+    grid.  With ``shared_qk=False`` the video keys get their own noise
+    (drawn after the query noise) instead of equalling the queries."""
     rng = np.random.Generator(np.random.PCG64(seed))
     P = prefix_len
     pre = [rng.standard_normal((B, P, H, D), dtype=np.float32) for _ in range(3)]
@@ -196,10 +220,11 @@ def h3_joint(B: int, N: int, H: int, D: int, prefix_len: int, seed: int):
         return 2.0 * math.pi * (f * inv[0][None] + y * inv[1][None] + x * inv[2][None]) + ph[None]
 
     s = _sum_of_sines(ang, nvid, H, D)
-    qk_vid = _signal_plus_noise(rng, s, B)
+    qk_vid = _signal_plus_noise(rng, s, B, amp)
+    k_vid = qk_vid if shared_qk else _signal_plus_noise(rng, s, B, amp)
     v_vid = _bf16(rng.standard_normal((B, nvid, H, D), dtype=np.float32))
     q = np.concatenate([_bf16(pre[0]), qk_vid], axis=1)
-    k = np.concatenate([_bf16(pre[1]), qk_vid], axis=1)
+    k = np.concatenate([_bf16(pre[1]), k_vid], axis=1)
     v = np.concatenate([_bf16(pre[2]), v_vid], axis=1)
     return q, k, v
 

@@ -262,6 +262,7 @@ def attend_block(
     logmass: bool,
     cbias_head: Optional[np.ndarray] = None,
     int8_head: Optional[dict] = None,
+    share: Optional[list] = None,
 ) -> np.ndarray:
     """Output rows of one query block of one head.
 
@@ -272,6 +273,8 @@ def attend_block(
     centroid bias (reweight mode) in place of log(n_c).  int8_head, when
     given, holds this head's INT8 QK^T quantities (qcode, qscale for these
     rows; kbase, kscale, kcode of the head) and sets the exact logits.
+    ``share``, when given, receives per row the centroid terms' share of the
+    softmax weight (float64 [n_a]; 0 without centroid terms).
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     chosen = np.nonzero(sel_row)[0]
@@ -297,9 +300,14 @@ def attend_block(
     L = np.concatenate(logits, axis=1)
     Vall = np.concatenate(values, axis=0)
     if L.shape[1] == 0:
+        if share is not None:
+            share.append(np.zeros(q_rows.shape[0]))
         return np.zeros((q_rows.shape[0], q_rows.shape[1]))
     M = L.max(axis=1, keepdims=True)
     W = np.exp(L - M)
+    if share is not None:
+        n_exact = logits[0].shape[1]
+        share.append(W[:, n_exact:].sum(axis=1) / W.sum(axis=1))
     return (W @ Vall) / W.sum(axis=1, keepdims=True)
 
 
@@ -431,12 +439,15 @@ def forward_blocks(
     sm_scale: Optional[float] = None,
     mask: Optional[np.ndarray] = None,
     info: Optional[dict] = None,
+    shares: Optional[dict] = None,
 ):
     """Output of selected (b, h, query block) triples, one by one.
 
     q, k, v: [B, N, H, D] bf16-exact values.  ``mask`` (bool [B,H,n_b,n_b])
     replaces the routing step when given.  ``info`` lets a caller reuse the
     pooled tensors and routing of an earlier call on the same inputs.
+    ``shares``, when given, receives {(b, h, a): per-row centroid share of
+    the softmax weight} (see attend_block).
     Returns ({(b, h, a): float64 [n_a, D]}, info).
     """
     B, N, H, D = q.shape
@@ -455,6 +466,7 @@ def forward_blocks(
     out = {}
     for b, h, a in blocks:
         rows = slice(a * BLOCK, a * BLOCK + sizes[a])
+        sh = [] if shares is not None else None
         out[(b, h, a)] = attend_block(
             q[b, rows, h, :],
             k[b, :, h, :],
@@ -468,7 +480,10 @@ def forward_blocks(
             logmass=logmass,
             cbias_head=info["cbias"][b, h] if reweight else None,
             int8_head=_int8_head(info["int8"], b, h, rows) if int8_qk else None,
+            share=sh,
         )
+        if shares is not None:
+            shares[(b, h, a)] = sh[0]
     return out, info
 
 

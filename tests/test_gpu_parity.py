@@ -6,7 +6,7 @@ Bars:
 * selected-block lists: bit-exact against the oracle's routing, except
   blocks within 1e-4 standard deviations of the row's cut (the tau
   threshold, or in top-K mode the midpoint between the k-th and (k+1)-th
-  scores), which must be under 0.1% of the routed blocks;
+  scores), which must be under 0.1% of all blocks of the call;
 * output, computed by the oracle on the GPU's own lists: max-abs <= 2e-2,
   mean-abs <= 2e-3, cosine >= 0.9995 (bf16 output vs fp64).
 
@@ -60,26 +60,34 @@ class GpuRun:
         return self.out.float().cpu().numpy().astype(np.float64)
 
     def selection(self):
-        counts, lists = self.plan.route_views(self.ws)
-        counts = counts.cpu().numpy()
-        lists = lists.cpu().numpy()
-        B, H, nb = counts.shape
-        assert ((counts >= 0) & (counts <= nb)).all()
-        valid = np.arange(nb)[None, None, None, :] < counts[..., None]
-        ent = np.where(valid, lists, -1)
-        assert ((ent[valid] >= 0) & (ent[valid] < nb)).all()
-        # ascending and distinct within each list
-        d = np.diff(np.where(valid, lists, np.iinfo(np.int32).max), axis=-1)
-        vv = valid[..., 1:]
-        assert (d[vv] > 0).all()
-        sel = np.zeros((B, H, nb, nb), dtype=bool)
-        bb, hh, aa, jj = np.nonzero(valid)
-        sel[bb, hh, aa, lists[bb, hh, aa, jj]] = True
-        return sel
+        return selection_from(*self.plan.route_views(self.ws))
+
+
+def selection_from(counts, lists):
+    """bool [B, H, n_b, n_b] from the library's counts and lists (checked:
+    counts in range, entries valid, ascending and distinct)."""
+    counts = counts.cpu().numpy()
+    lists = lists.cpu().numpy()
+    B, H, nb = counts.shape
+    assert ((counts >= 0) & (counts <= nb)).all()
+    valid = np.arange(nb)[None, None, None, :] < counts[..., None]
+    ent = np.where(valid, lists, -1)
+    assert ((ent[valid] >= 0) & (ent[valid] < nb)).all()
+    # ascending and distinct within each list
+    d = np.diff(np.where(valid, lists, np.iinfo(np.int32).max), axis=-1)
+    vv = valid[..., 1:]
+    assert (d[vv] > 0).all()
+    sel = np.zeros((B, H, nb, nb), dtype=bool)
+    bb, hh, aa, jj = np.nonzero(valid)
+    sel[bb, hh, aa, lists[bb, hh, aa, jj]] = True
+    return sel
 
 
 def check_route(sel_gpu, info, dense_rows_from=0):
-    """Lists equal the oracle's outside the 1e-4 sigma band; band < 0.1%."""
+    """Lists equal the oracle's except blocks within 1e-4 standard
+    deviations of their row's cut (|S - cut| <= 1e-4 sigma, the row's
+    population std of block scores); those must be under 0.1% of all blocks
+    of the call (B H n_b^2).  Returns that share."""
     ref = info["sel"]
     S, thr, sigma = info.get("S"), info["cut"], info["sigma"]
     diff = sel_gpu != ref
@@ -87,17 +95,15 @@ def check_route(sel_gpu, info, dense_rows_from=0):
         assert not diff.any()
         return 0.0
     routed = ~np.isnan(thr) & np.isfinite(thr)
-    scale = np.abs(S).max(axis=-1)
-    band = np.abs(S - thr[..., None]) <= (BAND_SIGMA * sigma + 1e-6 * scale)[..., None]
+    band = np.abs(S - thr[..., None]) <= (BAND_SIGMA * sigma)[..., None]
     band &= routed[..., None]
     bad = diff & ~band
-    n_routed = int(routed.sum()) * S.shape[-1]
-    frac = band.sum() / max(1, n_routed)
+    frac = band.sum() / S.size
     assert not bad.any(), f"{int(bad.sum())} selection mismatches outside the band, first at {np.argwhere(bad)[:5]}"
-    # The share bar needs at least 1000 routed blocks: below that, 0.1% is
-    # less than one block (a lone block always sits at its own row's cut).
-    if n_routed >= 1000:
-        assert frac < BAND_MAX_FRAC, f"band holds {frac:.2e} of routed blocks"
+    # The share bar needs at least 1000 blocks: below that, 0.1% is less
+    # than one block (a lone block always sits at its own row's cut).
+    if S.size >= 1000:
+        assert frac < BAND_MAX_FRAC, f"band holds {frac:.2e} of all blocks"
     return frac
 
 
@@ -362,17 +368,31 @@ def test_deterministic_reruns():
 
 
 def test_strided_fused_qkv_views():
-    """q, k, v as strided views of one [B, N, 3, H, D] projection output."""
+    """q, k, v as strided views of one [B, N, 3, H, D] projection output
+    (thakicloud accel-stack post, 이 기술은 무엇인가: strided views of the
+    fused qkv instead of copies), written into a strided output view: lists
+    and every output row against the oracle, the rest of the output buffer
+    untouched, and bit-identical to the same call on contiguous copies."""
     dev = _dev()
-    B, N, H, D = 1, 1100, 2, 128
-    q, k, v = inputs.clustered(B, N, H, D, seed=9)
+    B, N, H, D = 2, 1100, 2, 128
+    q, k, v = inputs.clustered_soft(B, N, H, D, seed=9)
     fused = np.stack([q, k, v], axis=2)  # [B, N, 3, H, D]
     ft = inputs.to_torch_bf16(fused, dev)
     tq, tk, tv = ft[:, :, 0], ft[:, :, 1], ft[:, :, 2]
-    out = binding.sparse_attn(tq, tk, tv, tau=1.0)
+    out_big = torch.zeros((B, N, 2, H, D), dtype=torch.bfloat16, device=dev)
+    out = out_big[:, :, 1]
+    kw = dict(tau=1.0, prefix_len=70)
+    _, counts, lists = binding.sparse_attn(tq, tk, tv, out=out, return_route=True, **kw)
     torch.cuda.synchronize()
-    ref_run = GpuRun(q, k, v, tau=1.0)
-    assert torch.equal(out.view(torch.int16), ref_run.out.view(torch.int16))
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    _, info = O.forward_blocks(qf, kf, vf, [], **kw)
+    sel = selection_from(counts, lists)
+    check_route(sel, info)
+    ref, _ = O.forward(qf, kf, vf, info=dict(info, sel=sel), **kw)
+    check_output(out.float().cpu().numpy().astype(np.float64), ref, "strided views")
+    assert (out_big[:, :, 0] == 0).all()
+    ref_run = GpuRun(q, k, v, **kw)
+    assert torch.equal(out.contiguous().view(torch.int16), ref_run.out.view(torch.int16))
 
 
 def test_injected_lists_through_attend():
@@ -483,6 +503,124 @@ def test_workload_h3_sampled():
 
 def test_workload_n32k_int8_sampled():
     _sampled_parity("n32k", n_sample=24, int8_qk=True)
+
+
+# ------------------------------------------------ soft softmax, full n_b
+#
+# With Q = K the diagonal key takes almost all of each row's softmax weight,
+# so the benchmarked workloads barely weigh the centroid terms.  These cases
+# draw keys independently of the queries (clustered_soft / the H3 layout with
+# its own key noise, amplitude 0.5): the routing still follows the signal,
+# but the unselected blocks' centroids carry most of the mass.  Every case
+# spans n_b >= 512 (16 to 19 centroid half tiles), and the oracle's own
+# centroid share of the sampled rows is asserted, so the output bars
+# measure the centroid path.
+
+SOFT = [
+    ("n32k_tau1", dict(gen="soft", N=32768, D=128), dict(tau=1.0)),
+    ("n32k_tau1_reweight", dict(gen="soft", N=32768, D=128), dict(tau=1.0, reweight=True)),
+    ("n32k_tau1_int8", dict(gen="soft", N=32768, D=128), dict(tau=1.0, int8_qk=True)),
+    ("n33000_d64_tau05", dict(gen="soft", N=33000, D=64), dict(tau=0.5)),
+    ("n33000_d64_topk_reweight", dict(gen="soft", N=33000, D=64), dict(topk_ratio=0.15, reweight=True)),
+    ("h3_topk", dict(gen="h3soft", N=38247, D=128), dict(topk_ratio=0.1, prefix_len=1024)),
+    ("h3_topk_reweight", dict(gen="h3soft", N=38247, D=128), dict(topk_ratio=0.1, prefix_len=1024, reweight=True)),
+    ("h3_topk_exact_kv", dict(gen="h3soft", N=38247, D=128), dict(topk_ratio=0.1, prefix_len=1024,
+                                                                  exact_kv_only=True)),
+]
+
+
+def _soft_inputs(gen, N, D, H=2, seed=50):
+    if gen == "soft":
+        return inputs.clustered_soft(1, N, H, D, seed=seed)
+    return inputs.h3_joint(1, N, H, D, prefix_len=1024, seed=seed, amp=0.5, shared_qk=False)
+
+
+@pytest.mark.parametrize("name,shape,kw", SOFT, ids=[s[0] for s in SOFT])
+def test_soft_softmax_full_nb_sampled(name, shape, kw):
+    q, k, v = _soft_inputs(shape["gen"], shape["N"], shape["D"], seed=50 + len(name))
+    run = GpuRun(q, k, v, **kw)
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    okw = oracle_kw(kw)
+    _, info = O.forward_blocks(qf, kf, vf, [], **okw)
+    sel = run.selection()
+    frac = check_route(sel, info)
+    B, N, H, D = q.shape
+    nb = O.num_blocks(N)
+    nct = -(-nb // 32)
+    pb = O.prefix_blocks(kw.get("prefix_len", 0))
+    rng = np.random.default_rng(7)
+    blocks = {(0, int(rng.integers(H)), int(rng.integers(pb, nb))) for _ in range(40)}
+    blocks |= {(0, 0, nb - 1), (0, 1, nb - 2), (0, 1, 0)}
+    if pb:
+        blocks |= {(0, 0, pb - 1), (0, 1, pb)}
+    blocks = sorted(blocks)
+    shares = {}
+    parts, _ = O.forward_blocks(qf, kf, vf, blocks, info=dict(info, sel=sel), shares=shares, **okw)
+    routed = [key for key in blocks if kw.get("exact_kv_only") or key[2] >= pb]
+    share = np.concatenate([shares[key] for key in routed])
+    # the unselected blocks of the sampled rows reach every centroid half
+    # tile, the ragged tail's centroid included
+    tiles = set()
+    tail_missed = 0
+    for b, h, a in routed:
+        missed = np.nonzero(~sel[b, h, a])[0]
+        tiles |= set((missed // 32).tolist())
+        tail_missed += int(not sel[b, h, a, nb - 1])
+    print(f"  {name}: density {sel.mean():.4f} band {frac:.2e} centroid share median {np.median(share):.3f} "
+          f"p10 {np.percentile(share, 10):.3f}; centroid half tiles reached {len(tiles)}/{nct}; "
+          f"tail centroid in {tail_missed} sampled rows", flush=True)
+    assert np.median(share) > 0.3, "the centroid terms must carry a material share of the softmax weight"
+    assert tiles == set(range(nct)) and tail_missed > 0
+    got = run.out_f64()
+    g = np.concatenate([got[b, a * 64 : a * 64 + r.shape[0], h] for (b, h, a), r in parts.items()])
+    r = np.concatenate(list(parts.values()))
+    check_output(g, r, f"{name} ({len(parts)} blocks)")
+
+
+@pytest.mark.parametrize("N,density", [(8192, 0.5), (32768, 0.35)])
+def test_injected_lists_full_nb(N, density):
+    """Caller-written random lists at n_b = 128 and 512 on soft inputs: the
+    pair unions run past 64 half tiles (the kernel's union table is refilled
+    every 64), with empty and full rows; every sampled row against the oracle
+    on the same mask."""
+    dev = _dev()
+    B, H, D = 1, 2, 128
+    q, k, v = inputs.clustered_soft(B, N, H, D, seed=N)
+    plan = binding.SparseAttnPlan(B, N, H, D, tau=1.0)
+    tq, tk, tv = (inputs.to_torch_bf16(x, dev) for x in (q, k, v))
+    ws = plan.workspace(dev)
+    plan.pool(tq, tk, tv, ws)
+    nb = plan.layout["n_blocks"]
+    rng = np.random.default_rng(N)
+    sel = rng.random((B, H, nb, nb)) < density
+    sel[0, 0, 3] = False  # nothing exact
+    sel[0, 1, 5] = True   # fully exact
+    sel[0, 0, 10] = False
+    sel[0, 0, 10, nb - 1] = True  # only the last block exact
+    counts, lists = plan.route_views(ws)
+    cnt = sel.sum(-1).astype(np.int32)
+    lst = np.zeros((B, H, nb, nb), dtype=np.int32)
+    for h in range(H):
+        for a in range(nb):
+            idx = np.nonzero(sel[0, h, a])[0]
+            lst[0, h, a, : len(idx)] = idx
+    counts.copy_(torch.from_numpy(cnt))
+    lists.copy_(torch.from_numpy(lst))
+    out = torch.empty_like(tq)
+    plan.attend(tq, out, ws)
+    torch.cuda.synchronize()
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    blocks = sorted({(0, h, a) for h in range(H) for a in (0, 3, 5, 10, 11, nb - 1)}
+                    | {(0, int(rng.integers(H)), int(rng.integers(nb))) for _ in range(24)})
+    shares = {}
+    parts, _ = O.forward_blocks(qf, kf, vf, blocks, mask=sel, shares=shares)
+    share = np.concatenate(list(shares.values()))
+    print(f"  injected N={N}: centroid share median {np.median(share):.3f}", flush=True)
+    assert np.median(share) > 0.1
+    got = out.float().cpu().numpy().astype(np.float64)
+    g = np.concatenate([got[b, a * 64 : a * 64 + r.shape[0], h] for (b, h, a), r in parts.items()])
+    r = np.concatenate(list(parts.values()))
+    check_output(g, r, f"injected N={N} ({len(parts)} blocks)")
 
 
 # ------------------------------------------------------------- Spark-Reblock
