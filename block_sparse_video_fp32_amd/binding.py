@@ -32,6 +32,7 @@ __all__ = [
     "SA_FLAG_REWEIGHT",
     "SA_FLAG_INT8_QK",
     "SA_FLAG_REBLOCK",
+    "SA_NOALLOC_SCRATCH_BYTES",
 ]
 
 SA_ROUTE_TAU = 0
@@ -42,6 +43,7 @@ SA_FLAG_EXACT_KV_ONLY = 4
 SA_FLAG_REWEIGHT = 8
 SA_FLAG_INT8_QK = 16
 SA_FLAG_REBLOCK = 32
+SA_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libsparse_attn.so"
@@ -153,6 +155,8 @@ def load_library() -> ctypes.CDLL:
         lib.sparse_attn_strerror.restype = ctypes.c_char_p
         lib.sparse_attn_last_error.argtypes = []
         lib.sparse_attn_last_error.restype = ctypes.c_char_p
+        lib.sparse_attn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp]
+        lib.sparse_attn_forward_noalloc.restype = i32
         lib.sparse_attn_abi_version.argtypes = []
         lib.sparse_attn_abi_version.restype = i32
         _lib = lib
@@ -324,6 +328,19 @@ class SparseAttnPlan:
         ws = self.workspace(q.device) if ws is None else ws
         self._call(self._lib.sparse_attn_forward, "sparse_attn_forward", q.device,
                    _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws), ws.numel())
+        return out
+
+    def forward_noalloc(self, q, k, v, out=None):
+        """sparse_attn_forward_noalloc: the full forward on the library's
+        per-device scratch array (no workspace; refused with SA_EWORKSPACE
+        when the plan needs more than SA_NOALLOC_SCRATCH_BYTES)."""
+        import torch
+
+        if out is None:
+            out = torch.empty_like(q)
+        self._check_io(ins=(q, k, v), outs=(out,))
+        self._call(self._lib.sparse_attn_forward_noalloc, "sparse_attn_forward_noalloc", q.device,
+                   _ptr(q), _ptr(k), _ptr(v), _ptr(out))
         return out
 
     def pool(self, q, k, v, ws=None):

@@ -449,4 +449,24 @@ int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void*
   return ok();
 }
 
+// The per-device scratch array lives in sparse_attn_noalloc.hip (a device
+// variable must be defined in device code); this returns its device address
+// for the current device, looked up once per device.
+__attribute__((visibility("hidden"))) int sparse_attn_noalloc_scratch(void** ptr);
+
+int sparse_attn_forward_noalloc(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
+                                void* out, void* stream) {
+  if (!plan) return fail(SA_EINVAL, "plan is NULL");
+  if (plan->layout.total_bytes > SA_NOALLOC_SCRATCH_BYTES)
+    return fail(SA_EWORKSPACE, "plan needs a %llu-byte workspace, the allocation-free scratch holds %llu",
+                (unsigned long long)plan->layout.total_bytes, (unsigned long long)SA_NOALLOC_SCRATCH_BYTES);
+  int rc;
+  if ((rc = check_tensors(q, k, v, out, true))) return rc;
+  if ((rc = check_device())) return rc;
+  void* ws = nullptr;
+  if ((rc = sparse_attn_noalloc_scratch(&ws)))
+    return fail(rc, "could not look up the device scratch array");
+  return sparse_attn_forward(plan, q, k, v, out, ws, (size_t)SA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 }  // extern "C"

@@ -295,6 +295,23 @@ int sparse_attn_route(const sparse_attn_plan* plan, const void* q, const void* k
 int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, void* out, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* Largest workspace the allocation-free entry point can serve (bytes of
+ * its per-device scratch array). */
+#define SA_NOALLOC_SCRATCH_BYTES (128ull << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as sparse_attn_forward, with the same arguments except the
+ * workspace, which is a library-owned scratch array of
+ * SA_NOALLOC_SCRATCH_BYTES bytes per device (held until the process ends).
+ * The call allocates and frees nothing.  Plans whose workspace_bytes exceed
+ * the array are refused with SA_EWORKSPACE before anything is launched.
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device race, so serialise them (one stream, or events between
+ * streams).  The array's contents on entry do not matter. */
+int sparse_attn_forward_noalloc(const sparse_attn_plan* plan, const void* q, const void* k, const void* v,
+                                void* out, void* stream);
+
 /* Static message for an error code.  Errors are reported, never repaired:
  * the Star7 README, section 环境与分发, stops the task on an architecture
  * mismatch with an error naming the required and detected capability and
