@@ -32,6 +32,7 @@ __all__ = [
     "SA_FLAG_REWEIGHT",
     "SA_FLAG_INT8_QK",
     "SA_FLAG_REBLOCK",
+    "SA_FLAG_REBLOCK_KV_OWN",
     "SA_NOALLOC_SCRATCH_BYTES",
 ]
 
@@ -43,6 +44,7 @@ SA_FLAG_EXACT_KV_ONLY = 4
 SA_FLAG_REWEIGHT = 8
 SA_FLAG_INT8_QK = 16
 SA_FLAG_REBLOCK = 32
+SA_FLAG_REBLOCK_KV_OWN = 64
 SA_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -209,6 +211,7 @@ class SparseAttnPlan:
         reweight: bool = False,
         int8_qk: bool = False,
         reblock: bool = False,
+        reblock_layout: str = "q_reuse_k",
         sm_scale: Optional[float] = None,
         in_strides: Optional[Tuple[int, int, int]] = None,
         out_strides: Optional[Tuple[int, int, int]] = None,
@@ -229,9 +232,12 @@ class SparseAttnPlan:
             p.tau = float(1.0 if tau is None else tau)
         p.prefix_len = int(prefix_len)
         p.sm_scale = float(sm_scale) if sm_scale else 0.0
+        if reblock_layout not in ("q_reuse_k", "separate"):
+            raise ValueError(f"reblock_layout must be 'q_reuse_k' or 'separate' (got {reblock_layout!r})")
         p.flags = ((SA_FLAG_CENTROID if centroid else 0) | (SA_FLAG_LOGMASS if logmass else 0)
                    | (SA_FLAG_EXACT_KV_ONLY if exact_kv_only else 0) | (SA_FLAG_REWEIGHT if reweight else 0)
-                   | (SA_FLAG_INT8_QK if int8_qk else 0) | (SA_FLAG_REBLOCK if reblock else 0))
+                   | (SA_FLAG_INT8_QK if int8_qk else 0) | (SA_FLAG_REBLOCK if reblock else 0)
+                   | (SA_FLAG_REBLOCK_KV_OWN if reblock and reblock_layout == "separate" else 0))
         handle = ctypes.c_void_p()
         _check(lib.sparse_attn_plan_create(ctypes.byref(p), ctypes.byref(handle)), "sparse_attn_plan_create")
         self._lib = lib
@@ -421,22 +427,24 @@ class SparseAttnPlan:
 
     def reblock_views(self, ws):
         """Spark-Reblock sections after ``forward`` with ``reblock=True``:
-        M fp32 [2, B, H, D, D] (side 0: K^T K for the query rows, side 1:
-        Q^T Q for the key rows), unit rows u and M u bf16 [2, B, H, n_v, D],
+        M fp32 [S, B, H, D, D] (side 0: K^T K for the query rows; side 1,
+        only in the separate layout: Q^T Q for the key rows), unit rows u and
+        M u bf16 [S, B, H, n_v, D], with S = 1 (q_reuse_k) or 2 (separate),
         and the orders perm_q, perm_k int64 [B, H, N] (new position i holds
-        input row perm[..., i])."""
+        input row perm[..., i]; in the q_reuse_k layout perm_k is perm_q)."""
         import torch
 
         B, N, H, D = self.shape
         r0 = min(self.layout["prefix_blocks"] * 64, N)
         nv = N - r0
-        M = self._view(ws, "rb_metric", torch.float32, (2, B, H, D, D))
-        U = self._view(ws, "rb_units", torch.bfloat16, (2, B, H, nv, D))
-        MU = self._view(ws, "rb_munits", torch.bfloat16, (2, B, H, nv, D))
-        ords = self._view(ws, "rb_order", torch.int32, (2, 2, B, H, nv))[self.layout["reblock_levels"] % 2]
+        S = 2 if self.params.flags & SA_FLAG_REBLOCK_KV_OWN else 1
+        M = self._view(ws, "rb_metric", torch.float32, (S, B, H, D, D))
+        U = self._view(ws, "rb_units", torch.bfloat16, (S, B, H, nv, D))
+        MU = self._view(ws, "rb_munits", torch.bfloat16, (S, B, H, nv, D))
+        ords = self._view(ws, "rb_order", torch.int32, (2, S, B, H, nv))[self.layout["reblock_levels"] % 2]
         head = torch.arange(r0, device=ws.device, dtype=torch.int64).expand(B, H, r0)
-        perms = [torch.cat([head, r0 + ords[side].to(torch.int64)], dim=2) for side in (0, 1)]
-        return M, U, MU, perms[0], perms[1]
+        perms = [torch.cat([head, r0 + ords[side].to(torch.int64)], dim=2) for side in range(S)]
+        return M, U, MU, perms[0], perms[-1]
 
     def int8_views(self, ws):
         """INT8 QK^T sections written by the pool step with ``int8_qk=True``:
@@ -467,6 +475,7 @@ def sparse_attn(
     reweight: bool = False,
     int8_qk: bool = False,
     reblock: bool = False,
+    reblock_layout: str = "q_reuse_k",
     sm_scale: Optional[float] = None,
     out=None,
     return_route: bool = False,
@@ -492,6 +501,7 @@ def sparse_attn(
         reweight=reweight,
         int8_qk=int8_qk,
         reblock=reblock,
+        reblock_layout=reblock_layout,
         logmass=logmass,
         sm_scale=sm_scale,
         in_strides=(q.stride(0), q.stride(1), q.stride(2)),

@@ -38,7 +38,8 @@ struct Shape {
   int rb_n;                 // reordered rows per (b, h), N - rb_r0
   int rb_levels;            // levels of the split tree
   int rb_chunks;            // partial second moments per problem
-  int rb_P;                 // problems: 2 sides x B x H
+  int rb_P;                 // problems: B x H (shared layout) or 2 sides x B x H
+  int rb_kv_own;            // keys and values take a partition of their own
   int permuted;             // the path reads Q, K, V rows (and writes output
                             // rows) through the final reblock orders
 };

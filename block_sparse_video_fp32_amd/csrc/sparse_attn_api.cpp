@@ -112,8 +112,12 @@ int validate_params(const sparse_attn_params& p) {
   if (p.H > 65535 || (int64_t)p.B * ((p.H + 7) / 8) > 65535)
     return fail(SA_EUNSUPPORTED_SHAPE, "B=%d, H=%d exceed the launch grid (H <= 65535, B*ceil(H/8) <= 65535)", p.B,
                 p.H);
-  if ((p.flags & SA_FLAG_REBLOCK) && 2 * (int64_t)p.B * p.H > 65535)
-    return fail(SA_EUNSUPPORTED_SHAPE, "SA_FLAG_REBLOCK needs 2*B*H <= 65535 (got B=%d, H=%d)", p.B, p.H);
+  if ((p.flags & SA_FLAG_REBLOCK_KV_OWN) && !(p.flags & SA_FLAG_REBLOCK))
+    return fail(SA_EINVAL, "SA_FLAG_REBLOCK_KV_OWN needs SA_FLAG_REBLOCK");
+  if ((p.flags & SA_FLAG_REBLOCK) &&
+      ((p.flags & SA_FLAG_REBLOCK_KV_OWN) ? 2 : 1) * (int64_t)p.B * p.H > 65535)
+    return fail(SA_EUNSUPPORTED_SHAPE, "SA_FLAG_REBLOCK needs %s <= 65535 (got B=%d, H=%d)",
+                (p.flags & SA_FLAG_REBLOCK_KV_OWN) ? "2*B*H" : "B*H", p.B, p.H);
   const bool in0 = p.in_stride_b == 0 && p.in_stride_t == 0 && p.in_stride_h == 0;
   const bool out0 = p.out_stride_b == 0 && p.out_stride_t == 0 && p.out_stride_h == 0;
   int rc;
@@ -134,7 +138,7 @@ int validate_params(const sparse_attn_params& p) {
     return fail(SA_EINVAL, "SA_FLAG_REWEIGHT needs SA_FLAG_CENTROID");
   if (p.flags &
       ~(SA_FLAG_CENTROID | SA_FLAG_LOGMASS | SA_FLAG_EXACT_KV_ONLY | SA_FLAG_REWEIGHT | SA_FLAG_INT8_QK |
-        SA_FLAG_REBLOCK))
+        SA_FLAG_REBLOCK | SA_FLAG_REBLOCK_KV_OWN))
     return fail(SA_EINVAL, "unknown flag bits 0x%x", p.flags);
   return SA_OK;
 }
@@ -190,7 +194,8 @@ void build_plan(sparse_attn_plan* pl) {
   s.rb_levels = 0;
   for (int m = (s.rb_n + sa::kBlock - 1) / sa::kBlock; (1 << s.rb_levels) < m;) ++s.rb_levels;
   s.rb_chunks = (p.N + sa::kGramChunk - 1) / sa::kGramChunk;
-  s.rb_P = 2 * p.B * p.H;
+  s.rb_kv_own = (p.flags & SA_FLAG_REBLOCK_KV_OWN) ? 1 : 0;
+  s.rb_P = (s.rb_kv_own ? 2 : 1) * p.B * p.H;
   s.permuted = 0;
 
   sparse_attn_ws_layout& L = pl->layout;
@@ -214,7 +219,7 @@ void build_plan(sparse_attn_plan* pl) {
   L.k_int8 = off; off = align256(off + (s.int8 ? bh * s.nb * 64ull * p.D : 0));
   L.kbase = off; off = align256(off + (s.int8 ? bh * s.nb * (uint64_t)(p.D + 8) * sizeof(uint16_t) : 0));
   const uint64_t rb = s.reblock ? 1 : 0;
-  const uint64_t P = 2 * bh, dd = (uint64_t)p.D * p.D;
+  const uint64_t P = (uint64_t)s.rb_P, dd = (uint64_t)p.D * p.D;
   L.rb_gram = off; off = align256(off + rb * P * s.rb_chunks * dd * sizeof(float));
   L.rb_metric = off; off = align256(off + rb * P * dd * sizeof(float));
   L.rb_units = off; off = align256(off + rb * P * s.rb_n * (uint64_t)p.D * sizeof(uint16_t));
@@ -306,11 +311,12 @@ void log_plan(const sparse_attn_plan* pl) {
     std::snprintf(route, sizeof(route), "tau %.4g", (double)p.tau);
   std::fprintf(stderr,
                "sparse_attn: plan B=%d N=%d H=%d D=%d n_b=%d tail=%d | %s | prefix %d rows (%d blocks, %s) | "
-               "centroid %d logmass %d reweight %d int8_qk %d reblock %d (%d levels) | scale %.6g | "
+               "centroid %d logmass %d reweight %d int8_qk %d reblock %d (%s, %d levels) | scale %.6g | "
                "workspace %.1f MiB\n",
                p.B, p.N, p.H, p.D, s.nb, s.tail, route, p.prefix_len, s.pb,
                s.prefix_rows ? "exact_kv_and_rows" : "exact_kv", s.centroid, (p.flags & SA_FLAG_LOGMASS) ? 1 : 0,
-               s.reweight, s.int8, s.reblock, s.reblock ? s.rb_levels : 0, (double)s.scale,
+               s.reweight, s.int8, s.reblock, s.rb_kv_own ? "separate" : "q_reuse_k", s.reblock ? s.rb_levels : 0,
+               (double)s.scale,
                (double)pl->layout.total_bytes / (1024.0 * 1024.0));
   std::fflush(stderr);
 }

@@ -74,10 +74,11 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as
 // Row of the caller's Q (side 0) or K and V (side 1) behind row r of (b, h)
 // on the path: with Spark-Reblock orders in use, row rb_r0 + i is the
 // caller's row rb_r0 + order[i] of the partition's final order (the prefix
-// blocks stay); otherwise r itself.
+// blocks stay; in the shared layout both sides use the query partition);
+// otherwise r itself.
 __device__ __forceinline__ int src_row(const Shape& s, const Workspace& ws, int side, long long bh, int r) {
   if (!s.permuted || r < s.rb_r0) return r;
-  const long long p = (long long)side * s.B * s.H + bh;
+  const long long p = (long long)(s.rb_kv_own ? side : 0) * s.B * s.H + bh;
   return s.rb_r0 + ws.rb_ord[((long long)(s.rb_levels & 1) * s.rb_P + p) * s.rb_n + (r - s.rb_r0)];
 }
 

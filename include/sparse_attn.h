@@ -55,7 +55,7 @@ extern "C" {
 
 #define SA_BLOCK 64          /* rows per query / key block */
 #define SA_MAX_BLOCKS 2048   /* largest supported n_b = ceil(N / 64) */
-#define SA_ABI_VERSION 5
+#define SA_ABI_VERSION 6
 
 /* Routing modes (sparse_attn_params.route). */
 #define SA_ROUTE_TAU 0   /* S >= mean + tau * std; tau = -inf is the dense path */
@@ -90,20 +90,26 @@ extern "C" {
  * and P V are unchanged.  Without it (the default) QK^T is bf16. */
 #define SA_FLAG_INT8_QK 16u
 /* Spark-Reblock (comfyui-wiki "Spark-H3" news, Spark-Reblock bullet): an
- * input-dependent block partition per (b, h).  Reading: queries are
- * partitioned in the metric M = K^T K (the cosine of their score patterns
- * over the keys), keys (with their values) in M = Q^T Q; rows after the
- * prefix blocks only.  Unit rows u = x / sqrt(x^T M x); a group of n > 64
- * rows splits into a left child of 64 ceil(ceil(n/64) / 2) rows and the
- * rest: pivot a = the row least similar (u^T M ubar) to the group's mean
- * direction, pivot b = the row least similar to a, and the left child takes
- * the rows ranked first by u^T M (u_b - u_a), ties by position; children
- * keep their parent's order.  The path then runs on Q, K, V in the new
- * orders, reading their rows through the orders, and writes every output
- * row at its own position.  sparse_attn_forward only (the
- * stage calls reject it); off on the dense path, whose result does not
- * depend on the order. */
+ * input-dependent block partition per (b, h).  Reading: the query rows after
+ * the prefix blocks are partitioned in the metric M = K^T K (the cosine of
+ * their score patterns over the keys), and the keys and values reuse that
+ * partition (the layout reblock_layout=q_reuse_k that the news's 워크플로
+ * section says every shipped workflow pins; SA_FLAG_REBLOCK_KV_OWN gives the
+ * keys a partition of their own instead).  Unit rows u = x / sqrt(x^T M x);
+ * a group of n > 64 rows splits into a left child of 64 ceil(ceil(n/64) / 2)
+ * rows and the rest: pivot a = the row least similar (u^T M ubar) to the
+ * group's mean direction, pivot b = the row least similar to a, and the left
+ * child takes the rows ranked first by u^T M (u_b - u_a), ties by position;
+ * children keep their parent's order.  The path then runs on Q, K, V in the
+ * new orders, reading their rows through the orders, and writes every
+ * output row at its own position.  sparse_attn_forward only (the stage
+ * calls reject it); off on the dense path, whose result does not depend on
+ * the order. */
 #define SA_FLAG_REBLOCK 32u
+/* With SA_FLAG_REBLOCK: the separate layout, in which the key rows (with
+ * their values) are partitioned on their own, in M = Q^T Q, by the same
+ * rule.  Without it the keys and values reuse the query partition. */
+#define SA_FLAG_REBLOCK_KV_OWN 64u
 #define SA_FLAGS_DEFAULT (SA_FLAG_CENTROID | SA_FLAG_LOGMASS)
 
 /* Error codes. */
@@ -111,7 +117,8 @@ extern "C" {
 #define SA_EINVAL (-1)              /* null pointer, bad parameter value */
 #define SA_EUNSUPPORTED_SHAPE (-2)  /* D not 64/128, n_b > SA_MAX_BLOCKS, B*H*n_b > 2^30,
                                        H > 65535, B*ceil(H/8) > 65535,
-                                       2*B*H > 65535 with SA_FLAG_REBLOCK */
+                                       B*H (2*B*H with SA_FLAG_REBLOCK_KV_OWN)
+                                       > 65535 with SA_FLAG_REBLOCK */
 #define SA_EUNSUPPORTED_DEVICE (-3) /* current device is not gfx950 */
 #define SA_EWORKSPACE (-4)          /* workspace smaller than required */
 #define SA_EALIGN (-5)              /* pointer or stride not 16-byte aligned */
@@ -171,7 +178,8 @@ typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
  *                     of D + 8 16-bit slots: the bf16 base row base_c, then
  *                     the fp32 block scale s_c in slots D, D + 1, then zero.
  * With SA_FLAG_REBLOCK only (problem p = side * B * H + b * H + h, side 0 =
- * query rows, side 1 = key rows; n_v = N - 64 * prefix_blocks rows move):
+ * query rows; side 1 = key rows exists with SA_FLAG_REBLOCK_KV_OWN only, so
+ * P = B H problems, or 2 B H with it; n_v = N - 64 * prefix_blocks rows move):
  *   rb_gram           fp32 partial second moments (scratch).
  *   rb_metric         fp32 [P, D, D]: M = Y^T Y of the other side.
  *   rb_units          bf16 [P, n_v, D]: the unit rows u of the moving rows.

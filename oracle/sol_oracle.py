@@ -59,8 +59,11 @@ What is computed, step by step, and where the pages state it:
    patterns over the keys are alike, measured by the cosine in the metric of
    the keys' second moment (and keys by that of the queries), and a
    hierarchical partitioner splits groups until every leaf has the block
-   size, in O(N log N).  Reading: per (b, h) and side, M = Y^T Y over all N
-   rows of the other side, u_i = x_i / sqrt(x_i^T M x_i) for the rows after
+   size, in O(N log N).  The shipped workflows pin the layout q_reuse_k
+   (same news, 워크플로 section): read as one partition per (b, h), made
+   for the queries, that the keys and values reuse.  Reading: per (b, h),
+   M = K^T K over all N keys (the "separate" layout also partitions the
+   keys on their own, in M = Q^T Q), u_i = x_i / sqrt(x_i^T M x_i) for the rows after
    the prefix blocks (prefix blocks stay in place), so that
    cos_M(x_i, x_j) = u_i^T M u_j; a group of n > 64 rows with m = ceil(n/64)
    blocks splits into a left child of 64 * ceil(m / 2) rows and the rest.
@@ -546,10 +549,15 @@ def _reblock_head(x, other, r0):
     return np.concatenate([np.arange(r0)] + [r0 + leaf for leaf in leaves]).astype(np.int64)
 
 
-def reblock_orders(q, k, prefix_len: int = 0):
+def reblock_orders(q, k, prefix_len: int = 0, layout: str = "q_reuse_k"):
     """Spark-Reblock orders (reading 7): perm_q, perm_k int64 [B, H, N];
     new position i of a head holds original row perm[..., i].  Queries use
-    M = K^T K, keys (and with them values) M = Q^T Q."""
+    M = K^T K.  layout "q_reuse_k" (the layout the shipped workflows pin,
+    Spark-H3 news, 워크플로 section) gives the keys, and with them the
+    values, the query partition: perm_k = perm_q.  layout "separate"
+    partitions the keys on their own, in M = Q^T Q."""
+    if layout not in ("q_reuse_k", "separate"):
+        raise ValueError(f"unknown reblock layout {layout!r}")
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     B, N, H, D = q.shape
@@ -559,7 +567,10 @@ def reblock_orders(q, k, prefix_len: int = 0):
     for b in range(B):
         for h in range(H):
             pq[b, h] = _reblock_head(q[b, :, h], k[b, :, h], r0)
-            pk[b, h] = _reblock_head(k[b, :, h], q[b, :, h], r0)
+            if layout == "q_reuse_k":
+                pk[b, h] = pq[b, h]
+            else:
+                pk[b, h] = _reblock_head(k[b, :, h], q[b, :, h], r0)
     return pq, pk
 
 
@@ -572,12 +583,13 @@ def _gather_rows(x, perm):
     return out
 
 
-def forward(q, k, v, reblock: bool = False, perms=None, **kw):
+def forward(q, k, v, reblock: bool = False, perms=None, reblock_layout: str = "q_reuse_k", **kw):
     """Full output [B, N, H, D] float64 plus the routing info.  With
     reblock=True the attention runs on the Spark-Reblock orders (``perms`` =
-    (perm_q, perm_k) to use given ones) and the rows are put back."""
+    (perm_q, perm_k) to use given ones, else reblock_orders with
+    ``reblock_layout``) and the rows are put back."""
     if reblock:
-        pq, pk = perms if perms is not None else reblock_orders(q, k, kw.get("prefix_len", 0))
+        pq, pk = perms if perms is not None else reblock_orders(q, k, kw.get("prefix_len", 0), reblock_layout)
         kw.pop("info", None)
         out_p, info = forward(_gather_rows(q, pq), _gather_rows(k, pk), _gather_rows(v, pk), **kw)
         out = np.empty_like(out_p)

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.sparse_attn_abi_version() == 5
+    assert lib.sparse_attn_abi_version() == 6
 
 
 def _params(**kw):
@@ -295,20 +295,23 @@ def test_int8_flag_is_accepted(lib):
     assert SA_FLAG_INT8_QK == 16
     for f in (3, 0, 3 | 8, 3 | 4):
         assert _create(lib, _params(flags=f | SA_FLAG_INT8_QK)) == 0
-    assert _create(lib, _params(flags=64)) == SA_EINVAL
+    assert _create(lib, _params(flags=128)) == SA_EINVAL
 
 
-def test_reblock_layout_and_stage_calls(lib):
-    """SA_FLAG_REBLOCK adds the partition sections (sizes as documented; the
-    copy sections rb_qkv and rb_out are empty) and runs through
-    sparse_attn_forward only: the stage calls refuse the plan
-    before touching any device."""
-    from block_sparse_video_fp32_amd.binding import SA_FLAG_REBLOCK
-    assert SA_FLAG_REBLOCK == 32
+@pytest.mark.parametrize("layout", ["q_reuse_k", "separate"])
+def test_reblock_layout_and_stage_calls(lib, layout):
+    """SA_FLAG_REBLOCK adds the partition sections (sizes as documented: one
+    problem per (b, h) in the shared q_reuse_k layout, two with
+    SA_FLAG_REBLOCK_KV_OWN; the copy sections rb_qkv and rb_out are empty)
+    and runs through sparse_attn_forward only: the stage calls refuse the
+    plan before touching any device."""
+    from block_sparse_video_fp32_amd.binding import SA_FLAG_REBLOCK, SA_FLAG_REBLOCK_KV_OWN
+    assert SA_FLAG_REBLOCK == 32 and SA_FLAG_REBLOCK_KV_OWN == 64
     B, N, H, D, pre = 2, 1000, 3, 128, 70
-    plan = binding.SparseAttnPlan(B, N, H, D, tau=1.0, prefix_len=pre, reblock=True)
+    plan = binding.SparseAttnPlan(B, N, H, D, tau=1.0, prefix_len=pre, reblock=True, reblock_layout=layout)
+    assert bool(plan.params.flags & SA_FLAG_REBLOCK_KV_OWN) == (layout == "separate")
     L = plan.layout
-    nv, P = N - 128, 2 * B * H
+    nv, P = N - 128, (2 if layout == "separate" else 1) * B * H
     assert L["reblock_levels"] == 4  # ceil(872 / 64) = 14 blocks
     sizes = dict(rb_gram=P * 1 * D * D * 4, rb_metric=P * D * D * 4, rb_units=P * nv * D * 2,
                  rb_munits=P * nv * D * 2, rb_order=2 * P * nv * 4, rb_keys=P * nv * 4, rb_qkv=0, rb_out=0)
@@ -316,6 +319,8 @@ def test_reblock_layout_and_stage_calls(lib):
     ends = [L[n] for n in names[1:]] + [L["total_bytes"]]
     for n, e in zip(names, ends):
         assert e - L[n] >= sizes[n], n
+    # sections sized for P problems, not more (the shared layout halves them)
+    assert L["rb_munits"] - L["rb_units"] < sizes["rb_units"] + 256
     # no reordered copies: the path reads its rows through the orders
     assert L["rb_qkv"] == L["rb_out"] and L["rb_out"] >= L["rb_keys"] + sizes["rb_keys"]
     dense = binding.SparseAttnPlan(B, N, H, D, tau=-math.inf, reblock=True)
@@ -327,6 +332,11 @@ def test_reblock_layout_and_stage_calls(lib):
                      (lib.sparse_attn_attend, (addr, addr, addr, 1 << 40, None))):
         assert fn(plan._h, *args) == SA_EINVAL
         assert "sparse_attn_forward" in lib.sparse_attn_last_error().decode()
+    # the separate layout is an option of SA_FLAG_REBLOCK only
+    assert _create(lib, _params(flags=3 | SA_FLAG_REBLOCK_KV_OWN)) == SA_EINVAL
+    assert "needs SA_FLAG_REBLOCK" in lib.sparse_attn_last_error().decode()
+    with pytest.raises(ValueError):
+        binding.SparseAttnPlan(B, N, H, D, reblock=True, reblock_layout="k_reuse_q")
 
 
 def test_workspace_bytes_and_route_entry_points(lib):
@@ -345,5 +355,8 @@ def test_launch_grid_limits(lib):
     assert _create(lib, _params(B=1, N=64, H=70000)) == SA_EUNSUPPORTED_SHAPE
     assert _create(lib, _params(B=70000, N=64, H=8)) == SA_EUNSUPPORTED_SHAPE
     assert _create(lib, _params(B=1, N=64, H=40000)) == 0
-    assert _create(lib, _params(B=1, N=64, H=40000, flags=3 | 32)) == SA_EUNSUPPORTED_SHAPE
+    assert _create(lib, _params(B=1, N=64, H=40000, flags=3 | 32)) == 0  # B*H problems
+    assert _create(lib, _params(B=2, N=64, H=40000, flags=3 | 32)) == SA_EUNSUPPORTED_SHAPE
     assert "REBLOCK" in lib.sparse_attn_last_error().decode()
+    assert _create(lib, _params(B=1, N=64, H=40000, flags=3 | 32 | 64)) == SA_EUNSUPPORTED_SHAPE
+    assert "2*B*H" in lib.sparse_attn_last_error().decode()

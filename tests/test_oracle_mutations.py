@@ -93,6 +93,10 @@ MUTATIONS = [
      "M = other.T @ other",
      "M = x.T @ x",
      [("test_reblock_metric_is_score_pattern_cosine", [()])]),
+    ("reblock_keys_own_partition",
+     "pk[b, h] = pq[b, h]",
+     "pk[b, h] = _reblock_head(k[b, :, h], q[b, :, h], r0)",
+     [("test_reblock_q_reuse_k_shares_the_query_partition", [()])]),
     ("pivot_a_most_similar",
      "a = int(np.argmin(s))",
      "a = int(np.argmax(s))",

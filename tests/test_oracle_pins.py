@@ -593,23 +593,51 @@ def test_pivot_split_hand_example():
 
 def test_reblock_recovers_planted_clusters():
     """Queries drawn tightly around four directions (two blocks each) in
-    shuffled positions: every leaf of the partition holds one cluster only,
-    and the prefix rows stay in place."""
+    shuffled positions, keys around four other directions with the same
+    labels by position: in the shared layout (q_reuse_k) every block holds
+    one cluster of queries and, since the keys reuse the query partition,
+    one cluster of keys; the prefix rows stay in place.  In the separate
+    layout the keys, labelled independently, get pure blocks of their own."""
     rng = np.random.default_rng(42)
     B, N, H, D, pre = 1, 64 + 512, 1, 32, 64
-    centers = rng.standard_normal((4, D))
+    cq, ck = rng.standard_normal((4, D)), rng.standard_normal((4, D))
     lab = np.repeat(np.arange(4), 128)
     rng.shuffle(lab)
     q = rng.standard_normal((B, N, H, D))
-    q[0, pre:, 0] = centers[lab] + 0.02 * rng.standard_normal((512, D))
+    q[0, pre:, 0] = cq[lab] + 0.02 * rng.standard_normal((512, D))
     k = rng.standard_normal((B, N, H, D))
+    k[0, pre:, 0] = ck[lab] + 0.02 * rng.standard_normal((512, D))
     pq, pk = O.reblock_orders(q, k, prefix_len=pre)
-    assert (pq[0, 0, :pre] == np.arange(pre)).all() and (pk[0, 0, :pre] == np.arange(pre)).all()
-    for perm in (pq, pk):
-        assert sorted(perm[0, 0].tolist()) == list(range(N))
-    blocks = (pq[0, 0, pre:] - pre).reshape(8, 64)
-    for blk in blocks:
+    assert (pk == pq).all()
+    assert (pq[0, 0, :pre] == np.arange(pre)).all()
+    assert sorted(pq[0, 0].tolist()) == list(range(N))
+    for blk in (pq[0, 0, pre:] - pre).reshape(8, 64):
         assert len(set(lab[blk].tolist())) == 1
+    labk = lab.copy()
+    rng.shuffle(labk)
+    k[0, pre:, 0] = ck[labk] + 0.02 * rng.standard_normal((512, D))
+    pq2, pk2 = O.reblock_orders(q, k, prefix_len=pre, layout="separate")
+    assert (pk2[0, 0, :pre] == np.arange(pre)).all()
+    for perm, lb in ((pq2, lab), (pk2, labk)):
+        assert sorted(perm[0, 0].tolist()) == list(range(N))
+        for blk in (perm[0, 0, pre:] - pre).reshape(8, 64):
+            assert len(set(lb[blk].tolist())) == 1
+
+
+def test_reblock_q_reuse_k_shares_the_query_partition():
+    """reblock_layout=q_reuse_k (Spark-H3 news, 워크플로 section): the keys and
+    values take the partition made for the queries (in M = K^T K), which is
+    also the separate layout's query partition; the separate layout's own key
+    partition (in M = Q^T Q) differs on generic inputs."""
+    q, k, v = _rand(2, 64 + 700, 2, 32, seed=46)
+    pq, pk = O.reblock_orders(q, k, prefix_len=64)
+    sq, sk = O.reblock_orders(q, k, prefix_len=64, layout="separate")
+    assert (pk == pq).all() and (sq == pq).all()
+    assert not (sk == pq).all()
+    a, info = O.forward(q, k, v, tau=1.0, prefix_len=64, reblock=True)
+    assert (info["perm_k"] == info["perm_q"]).all()
+    with pytest.raises(ValueError):
+        O.reblock_orders(q, k, layout="k_reuse_q")
 
 
 def test_reblock_leaves_do_not_depend_on_row_order():
