@@ -36,6 +36,7 @@ __all__ = [
     "SA_NOALLOC_SCRATCH_BYTES",
 ]
 
+SA_ABI_VERSION = 6  # include/sparse_attn.h
 SA_ROUTE_TAU = 0
 SA_ROUTE_TOPK = 1
 SA_FLAG_CENTROID = 1
@@ -161,6 +162,9 @@ def load_library() -> ctypes.CDLL:
         lib.sparse_attn_forward_noalloc.restype = i32
         lib.sparse_attn_abi_version.argtypes = []
         lib.sparse_attn_abi_version.restype = i32
+        got = lib.sparse_attn_abi_version()
+        if got != SA_ABI_VERSION:
+            raise ImportError(f"{path} has ABI version {got}, this binding needs {SA_ABI_VERSION}: rebuild the library")
         _lib = lib
         return lib
 

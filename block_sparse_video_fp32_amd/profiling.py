@@ -1,7 +1,9 @@
 """Summaries of rocprofv3 output for this library's kernels.
 
     # per-kernel call counts and durations from a --kernel-trace --stats run
-    python -m block_sparse_video_fp32_amd.profiling stats DIR
+    # (--skip N also averages each kernel's calls after its first N, e.g.
+    # the benchmark's warm-up calls)
+    python -m block_sparse_video_fp32_amd.profiling stats DIR [--skip N]
 
     # HBM bytes per attend launch from two --pmc runs (FETCH_SIZE, then
     # WRITE_SIZE) of a command that also ran a plain device copy of
@@ -48,16 +50,21 @@ def _find(dirname: str, suffix: str) -> str:
     return hits[0]
 
 
-def kernel_stats(dirname: str):
-    """Rows (name, calls, total_ns, avg_ns, min_ns, max_ns) from a kernel trace."""
+def kernel_stats(dirname: str, skip: int = 0):
+    """Rows (name, calls, total_ns, avg_ns, min_ns, max_ns, avg_ns after the
+    first `skip` calls or None) from a kernel trace, calls in start order."""
     path = _find(dirname, "kernel_trace.csv")
     per = collections.defaultdict(list)
     with open(path) as f:
         for r in csv.DictReader(f):
-            per[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            per[r["Kernel_Name"]].append((int(r["Start_Timestamp"]),
+                                          int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     rows = []
-    for name, d in per.items():
-        rows.append((name, len(d), sum(d), sum(d) / len(d), min(d), max(d)))
+    for name, calls in per.items():
+        d = [x for _, x in sorted(calls)]
+        rest = d[skip:]
+        rows.append((name, len(d), sum(d), sum(d) / len(d), min(d), max(d),
+                     sum(rest) / len(rest) if skip and rest else None))
     rows.sort(key=lambda r: -r[2])
     return rows
 
@@ -225,6 +232,7 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     a = sub.add_parser("stats")
     a.add_argument("dir")
+    a.add_argument("--skip", type=int, default=0, help="also average each kernel's calls after its first N")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_dir")
     b.add_argument("write_dir")
@@ -242,9 +250,11 @@ def main(argv=None):
     c.add_argument("--out")
     args = ap.parse_args(argv)
     if args.cmd == "stats":
-        print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10}  kernel")
-        for name, n, tot, avg, mn, mx in kernel_stats(args.dir):
-            print(f"{n:6d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f} {tot / 1e6:10.3f}  {name[:110]}")
+        extra = f" {'avg_us>' + str(args.skip):>10}" if args.skip else ""
+        print(f"{'calls':>6} {'avg_us':>10}{extra} {'min_us':>10} {'max_us':>10} {'total_ms':>10}  kernel")
+        for name, n, tot, avg, mn, mx, rest in kernel_stats(args.dir, args.skip):
+            ex = (f" {rest / 1e3:10.2f}" if rest is not None else f" {'-':>10}") if args.skip else ""
+            print(f"{n:6d} {avg / 1e3:10.2f}{ex} {mn / 1e3:10.2f} {mx / 1e3:10.2f} {tot / 1e6:10.3f}  {name[:110]}")
     else:
         if args.cmd == "counters":
             res = counters(args.pmc_dir, args.kernel)

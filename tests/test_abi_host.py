@@ -39,6 +39,8 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert lib.sparse_attn_abi_version() == 6
+    # the binding's expected version is the header's
+    assert f"#define SA_ABI_VERSION {binding.SA_ABI_VERSION}" in open(HEADER).read()
 
 
 def _params(**kw):

@@ -70,3 +70,19 @@ def test_traffic_scales_by_the_copy(tmp_path):
     # the copy read 512 KiB for 1 MiB moved (scale 2) and wrote 1024 KiB (scale 1)
     assert res["FETCH_SIZE"]["bytes_per_launch"] == pytest.approx(100 * 1024 * 2.0)
     assert res["WRITE_SIZE"]["bytes_per_launch"] == pytest.approx(10 * 1024 * 1.0)
+
+
+def test_kernel_stats_skip_warmup(tmp_path):
+    """Averages over all calls and over the calls after the first N (in start
+    order, whatever the order of the trace rows)."""
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "x_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for t0, dur in ((300, 10), (100, 40), (200, 20), (400, 30)):  # first two by start: 40, 20
+            w.writerow([KERNEL, t0, t0 + dur])
+    (name, n, tot, avg, mn, mx, rest), = profiling.kernel_stats(str(tmp_path), skip=2)
+    assert n == 4 and tot == 100 and avg == 25 and mn == 10 and mx == 40
+    assert rest == pytest.approx(20.0)  # (10 + 30) / 2
+    assert profiling.kernel_stats(str(tmp_path))[0][6] is None
