@@ -26,7 +26,14 @@
 //                      the mean, then least similar to the first pivot), the
 //                      rank values (M u_j) . (u_b - u_a), an exact radix
 //                      select of the left child's size (ties by position)
-//                      and a stable two-way partition of the group's order
+//                      and a stable two-way partition of the group's order;
+//                      groups of at most 8 or 16 row steps keep their M u
+//                      rows in registers, so each row is read once a level
+//   wide_pass_kernel,  the same level for levels with too few groups to fill
+//   wide_select_kernel the chip: each pass spread over 1024-row chunks (the
+//                      first level's mean comes from the embed's chunk
+//                      sums), then one workgroup per group selects and
+//                      partitions
 // The path then reads Q, K, V rows through the final orders and writes each
 // output row at its own position (no reordered copies).
 #include <hip/hip_runtime.h>
@@ -44,6 +51,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRbBlock = 64;
+constexpr int kWideRows = 1024;      // rows per chunk workgroup of a wide split level
+constexpr int kWideMaxGroups = 128;  // a level is wide when groups x problems is below this
 
 __device__ __forceinline__ float bf(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -163,7 +172,8 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(Shape s, Workspace ws)
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void embed_kernel(Shape s, const uint16_t* __restrict__ q,
-                                                    const uint16_t* __restrict__ k, Workspace ws) {
+                                                    const uint16_t* __restrict__ k, Workspace ws,
+                                                    float* __restrict__ usum) {
   constexpr int LP = D + 8, TW = D / 64, NK = D / 16, QD = D / 4;
   __shared__ __attribute__((aligned(16))) uint16_t Mb[D * LP];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kRbBlock * LP];
@@ -192,6 +202,9 @@ __global__ __launch_bounds__(256) void embed_kernel(Shape s, const uint16_t* __r
   };
   if ((int)blockIdx.x * kEmbedRows < jend) fetch(blockIdx.x * kEmbedRows);
   const int r = tid >> 2, qd = tid & 3;  // the row and quarter this thread finishes
+  float us[QD];  // sum of this thread's bf16 u quarters (for usum)
+#pragma unroll
+  for (int d = 0; d < QD; ++d) us[d] = 0.0f;
   for (int j0 = blockIdx.x * kEmbedRows; j0 < jend; j0 += kRbBlock) {
     __syncthreads();
 #pragma unroll
@@ -242,12 +255,31 @@ __global__ __launch_bounds__(256) void embed_kernel(Shape s, const uint16_t* __r
         for (int e = 0; e < 4; ++e) {
           wu[e] = to_bf16(xs[d + 2 * e] * inv) | (to_bf16(xs[d + 2 * e + 1] * inv) << 16);
           wm[e] = to_bf16(ys[d + 2 * e] * inv) | (to_bf16(ys[d + 2 * e + 1] * inv) << 16);
+          us[d + 2 * e] += bf(wu[e] & 0xffffu);
+          us[d + 2 * e + 1] += bf(wu[e] >> 16);
         }
         *reinterpret_cast<uint4*>(U + (long long)(j0 + r) * D + qd * QD + d) = make_uint4(wu[0], wu[1], wu[2], wu[3]);
         *reinterpret_cast<uint4*>(MU + (long long)(j0 + r) * D + qd * QD + d) = make_uint4(wm[0], wm[1], wm[2], wm[3]);
       }
       if (qd == 0) ord0[j0 + r] = j0 + r;
     }
+  }
+  // the chunk's sum of u (the bf16 values stored), for the mean direction
+  // of a wide first split level: over the 16 rows of a wave, then the waves
+  // in order
+  if (usum != nullptr) {
+#pragma unroll
+    for (int d = 0; d < QD; ++d)
+#pragma unroll
+      for (int o = 4; o < 64; o <<= 1) us[d] += __shfl_xor(us[d], o);
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(Xs);  // [4 waves][D]
+    if (lane < 4)
+#pragma unroll
+      for (int d = 0; d < QD; ++d) red[w * D + qd * QD + d] = us[d];
+    __syncthreads();
+    if (tid < D)
+      usum[((long long)p * gridDim.x + blockIdx.x) * D + tid] = red[tid] + red[D + tid] + red[2 * D + tid] + red[3 * D + tid];
   }
 }
 
@@ -282,24 +314,146 @@ __device__ __forceinline__ uint32_t order_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Stable two-way partition of a group's order (oin -> oout) by its rank
+// keys: the nl rows of smallest (key, position) go left in position order,
+// the others right.  T = the nl-th smallest key, by an exact radix select (8
+// bits at a time from the top); `want` ends as the rank, among the keys equal
+// to T, of the last one that goes left.  Each wave then walks a contiguous
+// segment of positions twice: once to count its left rows and its keys equal
+// to T, and, after one barrier, to place its rows.
+template <int NT>
+__device__ void select_partition(const uint32_t* __restrict__ keys, int n, int nl, const int* __restrict__ oin,
+                                 int* __restrict__ oout, uint32_t* hist, int* sel, int (*wc)[NT / 64]) {
+  constexpr int NWV = NT / 64;
+  constexpr int UN = 4;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t prefix = 0u;
+  int want = nl - 1;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+    __syncthreads();
+    const uint32_t mask = (shift == 24) ? 0u : (~0u << (shift + 8));
+    for (int j0 = tid; j0 < n; j0 += NT * UN) {
+      uint32_t kk[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) kk[u] = (j0 + u * NT < n) ? keys[j0 + u * NT] : 0u;
+#pragma unroll
+      for (int u = 0; u < UN; ++u)
+        if (j0 + u * NT < n && (kk[u] & mask) == prefix) atomicAdd(&hist[(kk[u] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wv == 0) {
+      const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+      const int cnt = (int)(h0 + h1 + h2 + h3);
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const int excl = incl - cnt;
+      if (excl <= want && want < incl) {
+        int r = want - excl, d = 4 * lane;
+        const uint32_t hs[4] = {h0, h1, h2, h3};
+        for (int i = 0; i < 3 && r >= (int)hs[i]; ++i) {
+          r -= (int)hs[i];
+          ++d;
+        }
+        sel[0] = d;
+        sel[1] = r;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sel[0] << shift;
+    want = sel[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+
+  const int seg = (((n + NWV - 1) / NWV) + 63) & ~63;
+  const int j0 = min(n, wv * seg), j1 = min(n, j0 + seg);
+  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int cl = 0, ce = 0;
+  for (int b0 = j0; b0 < j1; b0 += 64 * UN) {
+    uint32_t kk[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = b0 + 64 * u + lane;
+      kk[u] = (j < j1) ? keys[j] : 0xffffffffu;
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const bool in = b0 + 64 * u + lane < j1;
+      cl += __popcll(__ballot(in && kk[u] < T));
+      ce += __popcll(__ballot(in && kk[u] == T));
+    }
+  }
+  if (lane == 0) {
+    wc[0][wv] = cl;
+    wc[1][wv] = ce;
+  }
+  __syncthreads();
+  int L = 0, E = 0;
+  for (int i = 0; i < wv; ++i) {
+    L += wc[0][i];
+    E += wc[1][i];
+  }
+  // L counts the rows below T before the segment; add the equal keys that
+  // go left before it
+  L += min(E, want + 1);
+  for (int b0 = j0; b0 < j1; b0 += 64 * UN) {
+    uint32_t kk[UN];
+    int oi[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = b0 + 64 * u + lane;
+      kk[u] = (j < j1) ? keys[j] : 0xffffffffu;
+      oi[u] = (j < j1) ? oin[j] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = b0 + 64 * u + lane;
+      const bool in = j < j1;
+      const bool eq = in && kk[u] == T;
+      const unsigned long long be = __ballot(eq);
+      const bool left = in && (kk[u] < T || (eq && E + __popcll(be & lt_mask) <= want));
+      const unsigned long long bl = __ballot(left);
+      const int lrank = L + __popcll(bl & lt_mask);  // left rows before position j
+      if (in) oout[left ? lrank : nl + (j - lrank)] = oi[u];
+      L += __popcll(bl);
+      E += __popcll(be);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // split: grid (2^level, problems), NT threads.  Node g of the level reads
 // its rows' order from buffer level & 1 and writes its children's order to
 // buffer (level + 1) & 1.  Rows are read D/8 lanes per row (one 16-byte
 // chunk each), so a wave covers 64 / (D/8) rows per step and a lane keeps
-// the 8 matching entries of the current vector in registers.
+// the 8 matching entries of the current vector in registers.  With KR > 0
+// (groups of at most KR steps of rows) the mean pass also loads every row's
+// M u chunk into registers, the two argmin passes and the key pass run from
+// there, and the keys stay in LDS: each row is read from memory once per
+// level.
 // ---------------------------------------------------------------------------
-template <int D, int NT>
+template <int D, int NT, int KR>
 __global__ __launch_bounds__(NT) void split_kernel(Shape s, int level, Workspace ws) {
   constexpr int CPR = D / 8;      // lanes per row
   constexpr int RPW = 64 / CPR;   // rows per wave step
   constexpr int NWV = NT / 64;    // waves
   constexpr int STEP = NWV * RPW;
+  constexpr bool STASH = KR > 0;  // row steps held per lane
+  constexpr int NK = STASH ? KR * STEP : 1;
+  // Row loops take UN steps at a time: the order entries first, then the
+  // rows, so that the loads of a step do not wait on the previous step.
+  constexpr int UN = 4;
   __shared__ float vec[D];
   __shared__ float wsum[NWV][D];
   __shared__ float rv[NWV];
   __shared__ int ri[NWV];
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t kst[NK];
   __shared__ int sel[2];
   __shared__ int wc[2][NWV];
   const int g = blockIdx.x, p = blockIdx.y, nv = s.rb_n, tid = threadIdx.x;
@@ -318,26 +472,51 @@ __global__ __launch_bounds__(NT) void split_kernel(Shape s, int level, Workspace
   const uint16_t* MU = ws.rb_MU + (long long)p * nv * D;
   uint32_t* keys = ws.rb_key + (long long)p * nv + start;
 
-  // Row loops take UN steps at a time: the order entries first, then the
-  // rows, so that the loads of a step do not wait on the previous step.
-  constexpr int UN = 4;
+  uint4 mst[STASH ? KR : 1];  // M u chunks of rows wv RPW + sub + i STEP
   // mean direction ubar (fp32)
   {
     float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j0 = wv * RPW + sub; j0 < n; j0 += STEP * UN) {
-      int idx[UN];
+    auto add = [&](const uint4& v) {
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int u = 0; u < UN; ++u) idx[u] = (j0 + u * STEP < n) ? oin[j0 + u * STEP] : -1;
-      uint4 v[UN];
+      for (int e = 0; e < 8; ++e) a[e] += bf((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+    };
+    if constexpr (STASH) {
 #pragma unroll
-      for (int u = 0; u < UN; ++u)
-        v[u] = idx[u] >= 0 ? *reinterpret_cast<const uint4*>(U + (long long)idx[u] * D + c8 * 8)
-                           : make_uint4(0u, 0u, 0u, 0u);
+      for (int i0 = 0; i0 < KR; i0 += UN) {
+        // positions past the group load its first row (in bounds) and are
+        // left out of the sums and of every later pass
+        int idx[UN];
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        for (int u = 0; u < UN; ++u) {
+          const int j = wv * RPW + sub + (i0 + u) * STEP;
+          idx[u] = oin[j < n ? j : 0];
+        }
+        uint4 v[UN];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] += bf((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        for (int u = 0; u < UN; ++u) {
+          v[u] = *reinterpret_cast<const uint4*>(U + (long long)idx[u] * D + c8 * 8);
+          mst[i0 + u] = *reinterpret_cast<const uint4*>(MU + (long long)idx[u] * D + c8 * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < UN; ++u)
+          if (wv * RPW + sub + (i0 + u) * STEP < n) add(v[u]);
+        // keep the next steps' loads after these sums: only UN u chunks
+        // are live at a time beside the stash
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      for (int j0 = wv * RPW + sub; j0 < n; j0 += STEP * UN) {
+        int idx[UN];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) idx[u] = (j0 + u * STEP < n) ? oin[j0 + u * STEP] : -1;
+        uint4 v[UN];
+#pragma unroll
+        for (int u = 0; u < UN; ++u)
+          v[u] = idx[u] >= 0 ? *reinterpret_cast<const uint4*>(U + (long long)idx[u] * D + c8 * 8)
+                             : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int u = 0; u < UN; ++u) add(v[u]);
       }
     }
 #pragma unroll
@@ -360,6 +539,20 @@ __global__ __launch_bounds__(NT) void split_kernel(Shape s, int level, Workspace
   auto take_vec = [&]() {
 #pragma unroll
     for (int e = 0; e < 8; ++e) gvec[e] = vec[c8 * 8 + e];
+    // each pass converts the stashed bf16 afresh: without this the compiler
+    // keeps the converted fp32 rows of all passes live (8 registers a row)
+    if constexpr (STASH)
+#pragma unroll
+      for (int i = 0; i < KR; ++i) asm volatile("" : "+v"(mst[i].x), "+v"(mst[i].y), "+v"(mst[i].z), "+v"(mst[i].w));
+  };
+  auto dot = [&](const uint4& v) {
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    float x = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x += bf((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu) * gvec[e];
+#pragma unroll
+    for (int o = 1; o < CPR; o <<= 1) x += __shfl_xor(x, o);
+    return x;
   };
   // UN steps of rows: dots (M u_j) . vec for group positions
   // j0 + u STEP + sub, in every lane of each row's lanes
@@ -373,30 +566,35 @@ __global__ __launch_bounds__(NT) void split_kernel(Shape s, int level, Workspace
       v[u] = idx[u] >= 0 ? *reinterpret_cast<const uint4*>(MU + (long long)idx[u] * D + c8 * 8)
                          : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      float x = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x += bf((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu) * gvec[e];
-#pragma unroll
-      for (int o = 1; o < CPR; o <<= 1) x += __shfl_xor(x, o);
-      t[u] = x;
-    }
+    for (int u = 0; u < UN; ++u) t[u] = dot(v[u]);
   };
   // smallest (value, position) over the group; ties to the lower position
   auto argmin_pass = [&]() {
     take_vec();
     float best = INFINITY;
     int bj = 0x7fffffff;
-    for (int j0 = wv * RPW; j0 < n; j0 += STEP * UN) {
-      float t[UN];
-      row_dots(j0, t);
+    if constexpr (STASH) {
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const int j = j0 + u * STEP + sub;
-        if (j < n && t[u] < best) {
-          best = t[u];
+      for (int i = 0; i < KR; ++i) {
+        const float t = dot(mst[i]);
+        const int j = wv * RPW + sub + i * STEP;
+        if (j < n && t < best) {
+          best = t;
           bj = j;
+        }
+        if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // 4 rows' conversions live at a time
+      }
+    } else {
+      for (int j0 = wv * RPW; j0 < n; j0 += STEP * UN) {
+        float t[UN];
+        row_dots(j0, t);
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+          const int j = j0 + u * STEP + sub;
+          if (j < n && t[u] < best) {
+            best = t[u];
+            bj = j;
+          }
         }
       }
     }
@@ -438,29 +636,43 @@ __global__ __launch_bounds__(NT) void split_kernel(Shape s, int level, Workspace
   const int b = argmin_pass();  // least similar to a
   set_vec(a, b);                // u_b - u_a
   take_vec();
-  for (int j0 = wv * RPW; j0 < n; j0 += STEP * UN) {
-    float t[UN];
-    row_dots(j0, t);
+  // rank keys: in LDS with STASH, else in the workspace
+  uint32_t* kout = STASH ? kst : keys;
+  if constexpr (STASH) {
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int j = j0 + u * STEP + sub;
-      if (j < n && c8 == 0) keys[j] = order_bits(t[u]);
+    for (int i = 0; i < KR; ++i) {
+      const float t = dot(mst[i]);
+      const int j = wv * RPW + sub + i * STEP;
+      if (j < n && c8 == 0) kst[j] = order_bits(t);
+      if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (int j0 = wv * RPW; j0 < n; j0 += STEP * UN) {
+      float t[UN];
+      row_dots(j0, t);
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int j = j0 + u * STEP + sub;
+        if (j < n && c8 == 0) keys[j] = order_bits(t[u]);
+      }
     }
   }
   __syncthreads();
 
-  // Groups of at most NT rows: each row's rank (keys, then positions) by
+  // Groups of at most 256 rows: each row's rank (keys, then positions) by
   // comparison with every other row; the left child is the ranks < nl.
-  if (n <= NT) {
-    uint32_t* kl = hist;  // reused as the group's keys (n <= 256 here)
+  if (n <= 256) {
+    uint32_t* kl = STASH ? kst : hist;
     const bool in = tid < n;
-    const uint32_t key = in ? keys[tid] : 0u;
-    if (NT == 256 && in) kl[tid] = key;
-    __syncthreads();
+    const uint32_t key = in ? kout[tid] : 0u;
+    if (!STASH) {
+      if (in) kl[tid] = key;
+      __syncthreads();
+    }
     int rank = 0;
     if (in)
       for (int i = 0; i < n; ++i) {
-        const uint32_t ki = (NT == 256) ? kl[i] : keys[i];
+        const uint32_t ki = kl[i];
         rank += (ki < key || (ki == key && i < tid)) ? 1 : 0;
       }
     const bool left = in && rank < nl;
@@ -476,84 +688,202 @@ __global__ __launch_bounds__(NT) void split_kernel(Shape s, int level, Workspace
     }
     return;
   }
+  select_partition<NT>(kout, n, nl, oin, oout, hist, sel, wc);
+}
 
-  // T = the nl-th smallest key (radix select, 8 bits at a time from the
-  // top); `want` ends as its rank among the keys equal to T.
-  uint32_t prefix = 0u;
-  int want = nl - 1;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-    __syncthreads();
-    const uint32_t mask = (shift == 24) ? 0u : (~0u << (shift + 8));
-    for (int j = tid; j < n; j += NT) {
-      const uint32_t key = keys[j];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wv == 0) {
-      const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-      const int cnt = (int)(h0 + h1 + h2 + h3);
-      int incl = cnt;
+// ---------------------------------------------------------------------------
+// Wide split levels.  When a level has too few groups to fill the chip, each
+// group's row passes are spread over chunk workgroups of kWideRows rows:
+// grid (nch, 2^level, problems), 256 threads, one launch per pass.
+//   phase 0  partial sums of u over the chunk
+//   phase 1  the mean direction (the partials summed in chunk order), then
+//            the chunk's smallest (M u_j) . ubar and its position
+//   phase 2  a = the group's smallest of phase 1 (ties to the lower
+//            position), then the chunk's smallest (M u_j) . u_a
+//   phase 3  b likewise; the chunk's rank keys (M u_j) . (u_b - u_a)
+// wide_select_kernel then selects and partitions each group.  The row dots
+// are those of split_kernel, so only the mean's summation order differs
+// from a level run by one workgroup per group.  The partials live in the
+// rb_part section, which is free once M is reduced: sums [P][G][nch][D]
+// fp32, then two minima arrays [P][G][nch] of (value bits, position).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void wide_pass_kernel(Shape s, int level, int phase, int nch, Workspace ws) {
+  constexpr int NT = 256, CPR = D / 8, RPW = 64 / CPR, NWV = NT / 64, STEP = NWV * RPW, UN = 4;
+  __shared__ float vec[D];
+  __shared__ float wsum[NWV][D];
+  __shared__ float rv[NWV];
+  __shared__ int ri[NWV];
+  __shared__ int piv[2];
+  const int c = blockIdx.x, g = blockIdx.y, p = blockIdx.z, G = gridDim.y, nv = s.rb_n, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, sub = lane / CPR, c8 = lane % CPR;
+  int start, n;
+  group_range(nv, level, g, start, n);
+  if (n <= kRbBlock) return;  // leaves and empty nodes: the select kernel copies them
+  const int nc = (n + kWideRows - 1) / kWideRows;
+  if (c >= nc) return;
+  const int r0 = c * kWideRows, r1 = min(n, r0 + kWideRows);
+  const int* oin = ws.rb_ord + ((long long)(level & 1) * s.rb_P + p) * nv + start;
+  const uint16_t* U = ws.rb_U + (long long)p * nv * D;
+  const uint16_t* MU = ws.rb_MU + (long long)p * nv * D;
+  const long long pg = (long long)p * G + g;
+  float* sums = ws.rb_part + pg * nch * D;
+  int2* mins = reinterpret_cast<int2*>(ws.rb_part + (long long)s.rb_P * G * nch * D);
+  const long long mstride = (long long)s.rb_P * G * nch;
+
+  if (phase == 0) {
+    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j0 = r0 + wv * RPW + sub; j0 < r1; j0 += STEP * UN) {
+      int idx[UN];
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
-      const int excl = incl - cnt;
-      if (excl <= want && want < incl) {
-        int r = want - excl, d = 4 * lane;
-        const uint32_t hs[4] = {h0, h1, h2, h3};
-        for (int i = 0; i < 3 && r >= (int)hs[i]; ++i) {
-          r -= (int)hs[i];
-          ++d;
-        }
-        sel[0] = d;
-        sel[1] = r;
+      for (int u = 0; u < UN; ++u) idx[u] = (j0 + u * STEP < r1) ? oin[j0 + u * STEP] : -1;
+      uint4 v[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u)
+        v[u] = idx[u] >= 0 ? *reinterpret_cast<const uint4*>(U + (long long)idx[u] * D + c8 * 8)
+                           : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += bf((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
       }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int o = CPR; o < 64; o <<= 1) a[e] += __shfl_xor(a[e], o);
+    if (sub == 0)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wsum[wv][c8 * 8 + e] = a[e];
     __syncthreads();
-    prefix |= (uint32_t)sel[0] << shift;
-    want = sel[1];
-    __syncthreads();
+    if (tid < D) {
+      float t = 0.0f;
+      for (int i = 0; i < NWV; ++i) t += wsum[i][tid];
+      sums[(long long)c * D + tid] = t;
+    }
+    return;
   }
-  const uint32_t T = prefix;
 
-  // stable partition: keys < T, then the first want + 1 keys equal to T, go
-  // left (nl rows); the rest go right
-  int base_l = 0, base_e = 0;
-  for (int j0 = 0; j0 < n; j0 += NT) {
-    const int j = j0 + tid;
-    const bool in = j < n;
-    const uint32_t key = in ? keys[j] : 0xffffffffu;
-    const bool eq = in && key == T;
-    const unsigned long long be = __ballot(eq);
-    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int erank_w = __popcll(be & lt_mask);
-    if (lane == 0) wc[0][wv] = __popcll(be);
-    __syncthreads();
-    int eoff = 0, etot = 0;
-    for (int i = 0; i < NWV; ++i) {
-      if (i < wv) eoff += wc[0][i];
-      etot += wc[0][i];
+  // the group's smallest (value, position) over the chunk minima of an
+  // earlier phase; (value, position) pairs are distinct, so the result does
+  // not depend on the order of the comparisons
+  if (wv == 0) {
+    for (int which = 0; which < phase - 1; ++which) {
+      float best = INFINITY;
+      int bj = 0x7fffffff;
+      for (int i = lane; i < nc; i += 64) {
+        const int2 e = mins[which * mstride + pg * nch + i];
+        const float v = __int_as_float(e.x);
+        if (v < best || (v == best && e.y < bj)) {
+          best = v;
+          bj = e.y;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(best, o);
+        const int j2 = __shfl_xor(bj, o);
+        if (v2 < best || (v2 == best && j2 < bj)) {
+          best = v2;
+          bj = j2;
+        }
+      }
+      if (lane == 0) piv[which] = bj;
     }
-    const bool left = in && (key < T || (eq && base_e + eoff + erank_w <= want));
-    const unsigned long long bl = __ballot(left);
-    const int lrank_w = __popcll(bl & lt_mask);
-    if (lane == 0) wc[1][wv] = __popcll(bl);
-    __syncthreads();
-    int loff = 0, ltot = 0;
-    for (int i = 0; i < NWV; ++i) {
-      if (i < wv) loff += wc[1][i];
-      ltot += wc[1][i];
-    }
-    if (in) {
-      const int lrank = base_l + loff + lrank_w;  // left rows before j
-      oout[left ? lrank : nl + (j - lrank)] = oin[j];
-    }
-    base_l += ltot;
-    base_e += etot;
-    __syncthreads();
   }
+  __syncthreads();
+  if (tid < D) {
+    if (phase == 1) {
+      float t = 0.0f;
+      for (int i = 0; i < nc; ++i) t += sums[(long long)i * D + tid];
+      vec[tid] = t / (float)n;
+    } else {
+      const float xa = bf(U[(long long)oin[piv[0]] * D + tid]);
+      vec[tid] = (phase == 2) ? xa : bf(U[(long long)oin[piv[1]] * D + tid]) - xa;
+    }
+  }
+  __syncthreads();
+  float gvec[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gvec[e] = vec[c8 * 8 + e];
+  float best = INFINITY;
+  int bj = 0x7fffffff;
+  uint32_t* keys = ws.rb_key + (long long)p * nv + start;
+  for (int j0 = r0 + wv * RPW; j0 < r1; j0 += STEP * UN) {
+    int idx[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) idx[u] = (j0 + u * STEP + sub < r1) ? oin[j0 + u * STEP + sub] : -1;
+    uint4 v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u)
+      v[u] = idx[u] >= 0 ? *reinterpret_cast<const uint4*>(MU + (long long)idx[u] * D + c8 * 8)
+                         : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      float x = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x += bf((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu) * gvec[e];
+#pragma unroll
+      for (int o = 1; o < CPR; o <<= 1) x += __shfl_xor(x, o);
+      const int j = j0 + u * STEP + sub;
+      if (j < r1) {
+        if (phase == 3) {
+          if (c8 == 0) keys[j] = order_bits(x);
+        } else if (x < best) {
+          best = x;
+          bj = j;
+        }
+      }
+    }
+  }
+  if (phase == 3) return;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(best, o);
+    const int j2 = __shfl_xor(bj, o);
+    if (v2 < best || (v2 == best && j2 < bj)) {
+      best = v2;
+      bj = j2;
+    }
+  }
+  if (lane == 0) {
+    rv[wv] = best;
+    ri[wv] = bj;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float bv = rv[0];
+    int bb = ri[0];
+    for (int i = 1; i < NWV; ++i)
+      if (rv[i] < bv || (rv[i] == bv && ri[i] < bb)) {
+        bv = rv[i];
+        bb = ri[i];
+      }
+    mins[(phase - 1) * mstride + pg * nch + c] = make_int2(__float_as_int(bv), bb);
+  }
+}
+
+// wide_select: grid (2^level, problems), NT threads: copies the leaves and
+// partitions every other group of a wide level by the keys of phase 3.
+template <int NT>
+__global__ __launch_bounds__(NT) void wide_select_kernel(Shape s, int level, Workspace ws) {
+  __shared__ uint32_t hist[256];
+  __shared__ int sel[2];
+  __shared__ int wc[2][NT / 64];
+  const int g = blockIdx.x, p = blockIdx.y, nv = s.rb_n, tid = threadIdx.x;
+  int start, n;
+  group_range(nv, level, g, start, n);
+  if (n == 0) return;
+  const int* oin = ws.rb_ord + ((long long)(level & 1) * s.rb_P + p) * nv + start;
+  int* oout = ws.rb_ord + ((long long)((level + 1) & 1) * s.rb_P + p) * nv + start;
+  if (n <= kRbBlock) {
+    for (int i = tid; i < n; i += NT) oout[i] = oin[i];
+    return;
+  }
+  const int m = (n + kRbBlock - 1) / kRbBlock, nl = kRbBlock * ((m + 1) / 2);
+  select_partition<NT>(ws.rb_key + (long long)p * nv + start, n, nl, oin, oout, hist, sel, wc);
 }
 
 template <int D>
@@ -562,14 +892,39 @@ hipError_t partition_t(const Shape& s, const uint16_t* q, const uint16_t* k, con
   hipLaunchKernelGGL(gram_kernel<D>, dim3(s.rb_chunks, s.rb_P), dim3(256), 0, stream, s, q, k, ws);
   hipLaunchKernelGGL(gram_reduce_kernel<D>, dim3((D * D + 255) / 256, s.rb_P), dim3(256), 0, stream, s, ws);
   if (s.rb_n > 0) {
-    hipLaunchKernelGGL(embed_kernel<D>, dim3((s.rb_n + kEmbedRows - 1) / kEmbedRows, s.rb_P), dim3(256), 0, stream,
-                       s, q, k, ws);
+    const long long part_floats = (long long)s.rb_P * s.rb_chunks * D * D;
+    // a level is wide when its groups leave most of the chip idle; its
+    // partials then go to rb_part (free once M is reduced), which must hold
+    // them
+    auto is_wide = [&](int groups, int nch) {
+      return groups * s.rb_P < kWideMaxGroups && nch >= 2 && (long long)s.rb_P * groups * nch * (D + 4) <= part_floats;
+    };
+    static_assert(kEmbedRows == kWideRows, "an embed workgroup sums one chunk of the first wide level");
+    const int nch0 = (s.rb_n + kWideRows - 1) / kWideRows;
+    const bool wide0 = s.rb_levels > 0 && is_wide(1, nch0);
+    // with a wide first level the embed also writes its chunk sums of u (phase 0 of that level)
+    hipLaunchKernelGGL(embed_kernel<D>, dim3(nch0, s.rb_P), dim3(256), 0, stream, s, q, k, ws,
+                       wide0 ? ws.rb_part : nullptr);
     int biggest = s.rb_n;  // largest group of the level (the all-left node)
+    // rows per step of a 256-thread split workgroup; groups of up to 8 or 16
+    // steps keep their M u rows in registers
+    constexpr int kStep256 = 4 * (64 / (D / 8));
     for (int level = 0; level < s.rb_levels; ++level) {
-      if (biggest > 1024)
-        hipLaunchKernelGGL((split_kernel<D, 1024>), dim3(1u << level, s.rb_P), dim3(1024), 0, stream, s, level, ws);
-      else
-        hipLaunchKernelGGL((split_kernel<D, 256>), dim3(1u << level, s.rb_P), dim3(256), 0, stream, s, level, ws);
+      const int groups = 1 << level, nch = (biggest + kWideRows - 1) / kWideRows;
+      if (is_wide(groups, nch)) {
+        for (int phase = level == 0 ? 1 : 0; phase < 4; ++phase)
+          hipLaunchKernelGGL(wide_pass_kernel<D>, dim3(nch, groups, s.rb_P), dim3(256), 0, stream, s, level, phase,
+                             nch, ws);
+        hipLaunchKernelGGL(wide_select_kernel<1024>, dim3(groups, s.rb_P), dim3(1024), 0, stream, s, level, ws);
+      } else if (biggest > 1024) {
+        hipLaunchKernelGGL((split_kernel<D, 1024, 0>), dim3(1u << level, s.rb_P), dim3(1024), 0, stream, s, level, ws);
+      } else if (biggest > 16 * kStep256) {
+        hipLaunchKernelGGL((split_kernel<D, 256, 0>), dim3(1u << level, s.rb_P), dim3(256), 0, stream, s, level, ws);
+      } else if (biggest > 8 * kStep256) {
+        hipLaunchKernelGGL((split_kernel<D, 256, 16>), dim3(1u << level, s.rb_P), dim3(256), 0, stream, s, level, ws);
+      } else {
+        hipLaunchKernelGGL((split_kernel<D, 256, 8>), dim3(1u << level, s.rb_P), dim3(256), 0, stream, s, level, ws);
+      }
       if (biggest > kRbBlock) biggest = kRbBlock * (((biggest + kRbBlock - 1) / kRbBlock + 1) / 2);
     }
   }
