@@ -81,18 +81,33 @@ __device__ __forceinline__ const uint16_t* rows_of(const Shape& s, const Prob& p
 
 // ---------------------------------------------------------------------------
 // gram: grid (chunks, problems), 256 threads.  Wave w accumulates output
-// tiles (t / (D/32), t % (D/32)) for t = w, w + 4, ...; each 64-row
-// sub-chunk is staged as T[d][r] (bf16), so that the A operand
-// (A[i][k] = Y[k][32 ti + i]) and the B operand (B[k][j] = Y[k][32 tj + j])
-// are both 8 consecutive rows of one dimension.
+// tiles (t / (D/32), t % (D/32)) for t = w, w + 4, ...  Each 64-row
+// sub-chunk is staged row-major in LDS with 16-byte stores, and the MFMA
+// operands A[i][k] = Y[k][32 ti + i] and B[k][j] = Y[k][32 tj + j] come out
+// of it transposed by ds_read_b64_tr_b16: in each 16-lane group, lane 4a+e
+// receives element e of the 8-byte pieces addressed by lanes a, a+4, a+8 and
+// a+12 of the group.  So lane L = 16g + 4m + a addresses row k0 + 8(g/2) + m
+// (k0 + 4 more for the upper half of the operand) at column
+// 32 t + 16(g%2) + 4a, and every lane receives its operand's 8 rows of one
+// column in k order.
 // ---------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 lds_tr_frag(const uint16_t* p0, const uint16_t* p1) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p1));
+  const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void gram_kernel(Shape s, const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ k, Workspace ws) {
-  constexpr int TP = kRbBlock + 8;  // LDS pitch of T (elements)
+  constexpr int YP = D + 32;  // LDS pitch (elements): four consecutive rows cover all banks
   constexpr int NTD = D / 32;
   constexpr int TPW = NTD * NTD / 4;
-  __shared__ __attribute__((aligned(16))) uint16_t T[D * TP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[kRbBlock * YP];
   const int c = blockIdx.x, p = blockIdx.y;
   const Prob pr = prob_of(s, p);
   const uint16_t* y = rows_of(s, pr, q, k, true);
@@ -105,41 +120,48 @@ __global__ __launch_bounds__(256) void gram_kernel(Shape s, const uint16_t* __re
     ti[t] = (w + 4 * t) / NTD;
     tj[t] = (w + 4 * t) % NTD;
   }
+  // this lane's transposed-read address within a 16-row k step and a
+  // 32-column tile
+  const int g = lane >> 4, trow = 8 * (g >> 1) + ((lane >> 2) & 3), tcol = 16 * (g & 1) + 4 * (lane & 3);
   const int r_begin = c * kGramChunk, r_end = min(s.N, r_begin + kGramChunk);
-  // each thread stages LPT 16-byte chunks of a sub-chunk; the next
-  // sub-chunk is loaded into registers while the current one is multiplied
+  // each thread stages LPT 16-byte chunks of a sub-chunk; the sub-chunks
+  // two ahead are loaded into registers (two register sets in turn) while
+  // the current one is multiplied
   constexpr int LPT = kRbBlock * (D / 8) / 256;
-  uint4 nxt[LPT];
-  auto fetch = [&](int r0) {
+  uint4 na[LPT], nb[LPT];
+  auto fetch = [&](uint4(&dst)[LPT], int r0) {
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
       const int i = tid + 256 * u, r = i / (D / 8), c8 = i % (D / 8);
-      nxt[u] = (r0 + r < r_end) ? *reinterpret_cast<const uint4*>(y + (long long)(r0 + r) * s.ist + c8 * 8)
+      dst[u] = (r0 + r < r_end) ? *reinterpret_cast<const uint4*>(y + (long long)(r0 + r) * s.ist + c8 * 8)
                                 : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  if (r_begin < r_end) fetch(r_begin);
-  for (int r0 = r_begin; r0 < r_end; r0 += kRbBlock) {
+  auto step = [&](uint4(&cur)[LPT], int r0) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
       const int i = tid + 256 * u, r = i / (D / 8), c8 = i % (D / 8);
-      const uint32_t wv[4] = {nxt[u].x, nxt[u].y, nxt[u].z, nxt[u].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) T[(c8 * 8 + e) * TP + r] = (uint16_t)((wv[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+      *reinterpret_cast<uint4*>(Ys + r * YP + c8 * 8) = cur[u];
     }
     __syncthreads();
-    if (r0 + kRbBlock < r_end) fetch(r0 + kRbBlock);
+    if (r0 + 2 * kRbBlock < r_end) fetch(cur, r0 + 2 * kRbBlock);
 #pragma unroll
     for (int kk = 0; kk < kRbBlock / 16; ++kk) {
-      const int k0 = 16 * kk + 8 * hh;
+      const uint16_t* base = Ys + (16 * kk + trow) * YP + tcol;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(T + (32 * ti[t] + l32) * TP + k0);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(T + (32 * tj[t] + l32) * TP + k0);
+        const bf16x8 a = lds_tr_frag(base + 32 * ti[t], base + 4 * YP + 32 * ti[t]);
+        const bf16x8 b = lds_tr_frag(base + 32 * tj[t], base + 4 * YP + 32 * tj[t]);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
       }
     }
+  };
+  if (r_begin < r_end) fetch(na, r_begin);
+  if (r_begin + kRbBlock < r_end) fetch(nb, r_begin + kRbBlock);
+  for (int r0 = r_begin; r0 < r_end; r0 += 2 * kRbBlock) {
+    step(na, r0);
+    if (r0 + kRbBlock < r_end) step(nb, r0 + kRbBlock);
   }
   float* out = ws.rb_part + ((long long)p * s.rb_chunks + c) * D * D;
 #pragma unroll
@@ -190,30 +212,34 @@ __global__ __launch_bounds__(256) void embed_kernel(Shape s, const uint16_t* __r
   int* ord0 = ws.rb_ord + (long long)p * nv;
   const int rt = w & 1;
   const int jend = min(nv, (int)(blockIdx.x + 1) * kEmbedRows);
+  // the sub-chunks two ahead are loaded into registers (two register sets
+  // in turn) while the current one is processed
   constexpr int LPT = kRbBlock * (D / 8) / 256;
-  uint4 nxt[LPT];
-  auto fetch = [&](int j0) {
+  uint4 na[LPT], nb[LPT];
+  auto fetch = [&](uint4(&dst)[LPT], int j0) {
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
       const int i = tid + 256 * u, r = i / (D / 8), c8 = i % (D / 8);
-      nxt[u] = (j0 + r < nv) ? *reinterpret_cast<const uint4*>(x + (long long)(s.rb_r0 + j0 + r) * s.ist + c8 * 8)
+      dst[u] = (j0 + r < nv) ? *reinterpret_cast<const uint4*>(x + (long long)(s.rb_r0 + j0 + r) * s.ist + c8 * 8)
                              : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  if ((int)blockIdx.x * kEmbedRows < jend) fetch(blockIdx.x * kEmbedRows);
+  const int jbeg = blockIdx.x * kEmbedRows;
+  if (jbeg < jend) fetch(na, jbeg);
+  if (jbeg + kRbBlock < jend) fetch(nb, jbeg + kRbBlock);
   const int r = tid >> 2, qd = tid & 3;  // the row and quarter this thread finishes
   float us[QD];  // sum of this thread's bf16 u quarters (for usum)
 #pragma unroll
   for (int d = 0; d < QD; ++d) us[d] = 0.0f;
-  for (int j0 = blockIdx.x * kEmbedRows; j0 < jend; j0 += kRbBlock) {
+  auto step = [&](uint4(&cur)[LPT], int j0) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
       const int i = tid + 256 * u, rr = i / (D / 8), c8 = i % (D / 8);
-      *reinterpret_cast<uint4*>(Xs + rr * LP + c8 * 8) = nxt[u];
+      *reinterpret_cast<uint4*>(Xs + rr * LP + c8 * 8) = cur[u];
     }
     __syncthreads();
-    if (j0 + kRbBlock < jend) fetch(j0 + kRbBlock);
+    if (j0 + 2 * kRbBlock < jend) fetch(cur, j0 + 2 * kRbBlock);
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
       const int ct = (w >> 1) * TW + t;
@@ -263,6 +289,10 @@ __global__ __launch_bounds__(256) void embed_kernel(Shape s, const uint16_t* __r
       }
       if (qd == 0) ord0[j0 + r] = j0 + r;
     }
+  };
+  for (int j0 = jbeg; j0 < jend; j0 += 2 * kRbBlock) {
+    step(na, j0);
+    if (j0 + kRbBlock < jend) step(nb, j0 + kRbBlock);
   }
   // the chunk's sum of u (the bf16 values stored), for the mean direction
   // of a wide first split level: over the 16 rows of a wave, then the waves
