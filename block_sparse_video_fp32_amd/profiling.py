@@ -25,6 +25,12 @@
     python -m block_sparse_video_fp32_amd.profiling counters PMC_DIR \\
         --kernel "attend_kernel<128, 2, false, false>" --out FILE.json
 
+    # the launches of one stretch of a trace in start order, e.g. the
+    # Spark-Reblock partition of the last reblock call: from the last launch
+    # whose name holds FIRST up to the next one whose name holds STOP
+    python -m block_sparse_video_fp32_amd.profiling sequence DIR \
+        --first gram_kernel --stop pool_q_kernel
+
 The directories are rocprofv3 ``-d`` output directories written with
 ``--output-format csv``.
 """
@@ -67,6 +73,27 @@ def kernel_stats(dirname: str, skip: int = 0):
                      sum(rest) / len(rest) if skip and rest else None))
     rows.sort(key=lambda r: -r[2])
     return rows
+
+
+def launch_sequence(dirname: str, first: str, stop: str):
+    """[(short name, grid, duration_ns)] of the launches from the last one
+    whose name holds `first` up to (not including) the next one whose name
+    holds `stop`, in start order; grid is the x, y, z grid size in threads."""
+    path = _find(dirname, "kernel_trace.csv")
+    with open(path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    starts = [i for i, r in enumerate(rows) if first in r["Kernel_Name"]]
+    if not starts:
+        raise RuntimeError(f"no launch of {first}")
+    out = []
+    for r in rows[starts[-1]:]:
+        name = r["Kernel_Name"]
+        if out and stop in name:
+            break
+        short = name.replace("void ", "").replace("sa::(anonymous namespace)::", "").split("(")[0]
+        grid = tuple(int(r.get(f"Grid_Size_{a}", 1) or 1) for a in "XYZ")
+        out.append((short, grid, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return out
 
 
 def counter_per_dispatch(dirname: str, counter: str, kernel_substr: str):
@@ -244,6 +271,10 @@ def main(argv=None):
     m.add_argument("bench_json", help="file holding the JSON line bench.py printed in the counter run")
     m.add_argument("--kernel", default="attend_kernel<128, 2, false, false>")
     m.add_argument("--out")
+    q = sub.add_parser("sequence")
+    q.add_argument("dir")
+    q.add_argument("--first", required=True)
+    q.add_argument("--stop", required=True)
     c = sub.add_parser("counters")
     c.add_argument("pmc_dir")
     c.add_argument("--kernel", default="attend_kernel<128, 2, false, false>")
@@ -255,6 +286,12 @@ def main(argv=None):
         for name, n, tot, avg, mn, mx, rest in kernel_stats(args.dir, args.skip):
             ex = (f" {rest / 1e3:10.2f}" if rest is not None else f" {'-':>10}") if args.skip else ""
             print(f"{n:6d} {avg / 1e3:10.2f}{ex} {mn / 1e3:10.2f} {mx / 1e3:10.2f} {tot / 1e6:10.3f}  {name[:110]}")
+    elif args.cmd == "sequence":
+        seq = launch_sequence(args.dir, args.first, args.stop)
+        print(f"{'us':>9}  {'grid (threads)':>22}  kernel")
+        for name, grid, ns in seq:
+            print(f"{ns / 1e3:9.1f}  {str(grid):>22}  {name}")
+        print(f"{sum(ns for _, _, ns in seq) / 1e3:9.1f}  {'total':>22}")
     else:
         if args.cmd == "counters":
             res = counters(args.pmc_dir, args.kernel)

@@ -86,3 +86,33 @@ def test_kernel_stats_skip_warmup(tmp_path):
     assert n == 4 and tot == 100 and avg == 25 and mn == 10 and mx == 40
     assert rest == pytest.approx(20.0)  # (10 + 30) / 2
     assert profiling.kernel_stats(str(tmp_path))[0][6] is None
+
+
+def test_launch_sequence_takes_the_last_stretch(tmp_path):
+    """The launches from the last `first` kernel up to the next `stop`
+    kernel, in start order, with their grids and durations."""
+    d = tmp_path / "trace"
+    d.mkdir()
+    rows = [  # (name, start, duration, grid x)
+        ("void sa::(anonymous namespace)::gram_kernel<128>(sa::Shape)", 0, 5, 64),
+        ("void sa::(anonymous namespace)::split_kernel<128, 256, 8>(sa::Shape, int)", 10, 7, 256),
+        ("void sa::(anonymous namespace)::pool_q_kernel<128>(sa::Shape)", 20, 3, 64),
+        ("void sa::(anonymous namespace)::gram_kernel<128>(sa::Shape)", 100, 6, 64),
+        ("void sa::(anonymous namespace)::wide_pass_kernel<128>(sa::Shape, int)", 110, 9, 1024),
+        ("void sa::(anonymous namespace)::split_kernel<128, 256, 8>(sa::Shape, int)", 105, 8, 256),
+        ("void sa::(anonymous namespace)::pool_q_kernel<128>(sa::Shape)", 130, 3, 64),
+        ("void sa::(anonymous namespace)::attend_kernel<128, 2, false, false>(sa::Shape)", 140, 50, 256),
+    ]
+    with open(d / "x_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"])
+        for name, t0, dur, gx in rows:
+            w.writerow([name, t0, t0 + dur, gx, 56, 1])
+    seq = profiling.launch_sequence(str(tmp_path), "gram_kernel", "pool_q_kernel")
+    assert [(n, g, ns) for n, g, ns in seq] == [
+        ("gram_kernel<128>", (64, 56, 1), 6),
+        ("split_kernel<128, 256, 8>", (256, 56, 1), 8),
+        ("wide_pass_kernel<128>", (1024, 56, 1), 9),
+    ]
+    with pytest.raises(RuntimeError):
+        profiling.launch_sequence(str(tmp_path), "embed_kernel", "pool_q_kernel")
