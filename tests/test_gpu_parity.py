@@ -916,6 +916,10 @@ REBLOCK = [
     ("short", dict(B=1, N=100, H=2, D=64), dict(tau=1.0, prefix_len=40)),
     ("separate_tau_prefix_d64", dict(B=1, N=1100, H=2, D=64), dict(tau=1.0, prefix_len=100, layout="separate")),
     ("separate_topk_tail_b2", dict(B=2, N=777, H=1, D=128), dict(topk_ratio=0.25, prefix_len=64, layout="separate")),
+    # more than 1024 moving rows on few problems: the first levels run wide
+    # (1024-row chunks, the last one ragged), the deepest from registers
+    ("wide_d64_b2_prefix", dict(B=2, N=5000, H=3, D=64), dict(tau=1.0, prefix_len=200)),
+    ("wide_d128_separate_topk", dict(B=1, N=4500, H=2, D=128), dict(topk_ratio=0.2, prefix_len=64, layout="separate")),
 ]
 
 
