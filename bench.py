@@ -174,7 +174,7 @@ def main():
     ap.add_argument("--workload", default="n32k", choices=["tiny", "n4k", "n16k", "n32k", "h3"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--no-modes", action="store_true", help="skip the reweight, INT8 QK^T and reblock timings")
+    ap.add_argument("--no-modes", action="store_true", help="skip the reweight, INT8 QK^T, strided fused-QKV and reblock timings")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 256 MiB device copy before the steps (scales rocprofv3 byte counters)")
@@ -300,6 +300,34 @@ def main():
             print(f"# {name}: {m_call:.3f} ms/call (pool {m_pool:.3f}, attend {m_att:.3f})", file=sys.stderr,
                   flush=True)
             del mws, mplan
+        # Q, K, V as strided views of one fused [B, N, 3, H, D] projection
+        # output (no copies), same routing and output
+        fused = torch.stack([q, k, v], dim=2)
+        fq, fk, fv = fused[:, :, 0], fused[:, :, 1], fused[:, :, 2]
+        mplan = binding.SparseAttnPlan(B, N, H, D, prefix_len=w.prefix_len, in_strides=fq.stride()[:3], **rkw)
+        mws = mplan.workspace(dev)
+        for _ in range(2):
+            mplan.forward(fq, fk, fv, out=out, ws=mws)
+        torch.cuda.synchronize()
+        km = max(3, K // 2)
+        me = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(km)]
+        for i in range(km):
+            me[i][0].record(stream)
+            mplan.pool(fq, fk, fv, mws)
+            me[i][1].record(stream)
+            mplan.select(mws)
+            me[i][2].record(stream)
+            mplan.attend(fq, out, mws)
+            me[i][3].record(stream)
+        torch.cuda.synchronize()
+        m_call = sum(e[0].elapsed_time(e[3]) for e in me) / km
+        m_pool = sum(e[0].elapsed_time(e[1]) for e in me) / km
+        m_att = sum(e[2].elapsed_time(e[3]) for e in me) / km
+        modes["strided_qkv"] = {"ms_per_call": round(m_call, 4), "pool_ms": round(m_pool, 4), "attend_ms": round(m_att, 4),
+                                "attend_vs_default": round(t_att / m_att, 3)}
+        print(f"# strided_qkv: {m_call:.3f} ms/call (pool {m_pool:.3f}, attend {m_att:.3f})", file=sys.stderr,
+              flush=True)
+        del mws, mplan, fq, fk, fv, fused
         # Spark-Reblock runs through the forward call (the partition, then the
         # path reading Q, K, V rows through the final order and writing each
         # output row at its own position)
