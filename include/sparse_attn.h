@@ -321,7 +321,7 @@ int sparse_attn_forward_noalloc(const sparse_attn_plan* plan, const void* q, con
                                 void* out, void* stream);
 
 /* Static message for an error code.  Errors are reported, never repaired:
- * the Star7 README, section 环境与分发, stops the task on an architecture
+ * the Star7 README, section 环境与分发, stops the job on an architecture
  * mismatch with an error naming the required and detected capability and
  * no fallback backend, and its section 错误处理与日志 runs strict modes with
  * no fallback. */
