@@ -86,8 +86,10 @@ def selection_from(counts, lists):
 def check_route(sel_gpu, info, dense_rows_from=0):
     """Lists equal the oracle's except blocks within 1e-4 standard
     deviations of their row's cut (|S - cut| <= 1e-4 sigma, the row's
-    population std of block scores); those must be under 0.1% of all blocks
-    of the call (B H n_b^2).  Returns that share."""
+    population std of block scores).  The blocks this excuses (in the band
+    and different) must be under 0.1% of all blocks of the call (B H n_b^2)
+    where the call has at least 1000 blocks; the band itself must be under
+    0.1% where the call has at least 10^4 blocks.  Returns the band's share."""
     ref = info["sel"]
     S, thr, sigma = info.get("S"), info["cut"], info["sigma"]
     diff = sel_gpu != ref
@@ -99,10 +101,16 @@ def check_route(sel_gpu, info, dense_rows_from=0):
     band &= routed[..., None]
     bad = diff & ~band
     frac = band.sum() / S.size
+    excused = int((diff & band).sum())
     assert not bad.any(), f"{int(bad.sum())} selection mismatches outside the band, first at {np.argwhere(bad)[:5]}"
-    # The share bar needs at least 1000 blocks: below that, 0.1% is less
-    # than one block (a lone block always sits at its own row's cut).
+    # Below 1000 blocks 0.1% is less than one block (a lone block always
+    # sits at its own row's cut in top-K mode).  On continuous scores about
+    # 1e-4 of the blocks fall within 1e-4 sigma of a cut by chance, so on
+    # calls under 10^4 blocks one or two chance near-ties already exceed a
+    # 0.1% bar on the band itself; there the bar bounds what it excuses.
     if S.size >= 1000:
+        assert excused < BAND_MAX_FRAC * S.size, f"{excused} in-band mismatches of {S.size} blocks"
+    if S.size >= 10000:
         assert frac < BAND_MAX_FRAC, f"band holds {frac:.2e} of all blocks"
     return frac
 
@@ -1141,3 +1149,53 @@ def test_workload_h3_reblock_reweight_int8_sampled():
         g.append(got[b, pq[b, h, a * 64 : a * 64 + o.shape[0]], h])
         r.append(o)
     check_output(np.concatenate(g), np.concatenate(r), f"h3 reblock+reweight+int8 ({len(parts)} blocks)")
+
+
+# -------------------------------------------------- seeded random configurations
+#
+# Shapes, routing, prefix, scale and flags drawn from one seed per case
+# (N in [1, 64] for a quarter of the cases, else in [65, 2600]; i.i.d. or
+# soft clustered inputs), every
+# output row against the oracle with the same bars as above.
+
+def _random_config(seed):
+    rng = np.random.default_rng(1000 + seed)
+    B, H, D = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.choice([64, 128]))
+    N = int(rng.integers(1, 65)) if rng.random() < 0.25 else int(rng.integers(65, 2601))
+    kw = {}
+    if rng.random() < 0.6:
+        kw["tau"] = float(rng.choice([-0.5, 0.0, 0.5, 1.0, 2.5]))
+    else:
+        kw["topk_ratio"] = float(rng.choice([0.03, 0.2, 0.5, 1.0]))
+    if rng.random() < 0.5:
+        kw["prefix_len"] = int(rng.integers(0, N + 1))
+    if rng.random() < 0.2:
+        kw["sm_scale"] = float(rng.uniform(0.05, 0.2))
+    if rng.random() < 0.2:
+        kw["centroid"] = False
+    elif rng.random() < 0.3:
+        kw["reweight"] = True
+    if rng.random() < 0.2:
+        kw["logmass"] = False
+    if rng.random() < 0.25:
+        kw["int8_qk"] = True
+    if rng.random() < 0.2:
+        kw["exact_kv_only"] = True
+    reblock = rng.random() < 0.25
+    layout = "separate" if reblock and rng.random() < 0.5 else "q_reuse_k"
+    soft = N >= 256 and rng.random() < 0.5
+    return dict(B=B, N=N, H=H, D=D, soft=soft, reblock=reblock, layout=layout), kw
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_configurations(seed):
+    shape, kw = _random_config(seed)
+    B, N, H, D = shape["B"], shape["N"], shape["H"], shape["D"]
+    print(f"  seed {seed}: B={B} N={N} H={H} D={D} soft={shape['soft']} reblock={shape['reblock']} "
+          f"({shape['layout']}) {kw}", flush=True)
+    gen = inputs.clustered_soft if shape["soft"] else inputs.iid
+    q, k, v = gen(B, N, H, D, seed=seed + 7)
+    if shape["reblock"]:
+        reblock_parity(q, k, v, layout=shape["layout"], **kw)
+    else:
+        full_parity(q, k, v, **kw)
