@@ -174,6 +174,7 @@ def main():
     ap.add_argument("--workload", default="n32k", choices=["tiny", "n4k", "n16k", "n32k", "h3"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="also time the call replayed from a HIP graph")
     ap.add_argument("--no-modes", action="store_true", help="skip the reweight, INT8 QK^T, strided fused-QKV and reblock timings")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -248,6 +249,32 @@ def main():
 
     flops, density = selected_flops(plan, ws, N, D)
     nb = plan.layout["n_blocks"]
+
+    # the same call captured once into a HIP graph and replayed (the library
+    # only launches kernels on the caller's stream, so it captures as is)
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            plan.forward(q, k, v, out=out, ws=ws)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            plan.forward(q, k, v, out=out, ws=ws)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(K):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / K
+        print(f"# graph replay: {graph_ms:.3f} ms/call", file=sys.stderr, flush=True)
+        del graph
 
     # dense path of the same library on the same inputs
     dense_ms = None
@@ -386,6 +413,7 @@ def main():
         "density": round(density, 5),
         "selected_tflop_per_call": round(flops / 1e12, 4),
         "attend_mfma_per_launch": attend_mfma_count(plan, ws, D),
+        "graph_ms_per_call": None if graph_ms is None else round(graph_ms, 4),
         "dense_ms_per_call": None if dense_ms is None else round(dense_ms, 3),
         "speedup_vs_own_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
         "dense_equivalent_tflops": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),

@@ -1199,3 +1199,41 @@ def test_random_configurations(seed):
         reblock_parity(q, k, v, layout=shape["layout"], **kw)
     else:
         full_parity(q, k, v, **kw)
+
+
+# ------------------------------------------------------------ graph capture
+#
+# The library launches only kernels on the caller's stream (no memset, no
+# allocation, no synchronisation), so a forward call can be captured into a
+# HIP graph.  Each replay runs after eager work and a synchronisation and
+# must equal the eager call bit for bit.
+
+@pytest.mark.parametrize("kw", [dict(tau=1.0, prefix_len=100), dict(topk_ratio=0.2, reweight=True, int8_qk=True),
+                                dict(tau=1.0, prefix_len=70, reblock=True)],
+                         ids=["tau_prefix", "topk_reweight_int8", "reblock"])
+def test_graph_capture_replays_match_eager(kw):
+    dev = _dev()
+    B, N, H, D = 1, 3000, 4, 128
+    q, k, v = (inputs.to_torch_bf16(x, dev) for x in inputs.clustered_soft(B, N, H, D, seed=5))
+    plan = binding.SparseAttnPlan(B, N, H, D, **kw)
+    ws = plan.workspace(dev)
+    ref = plan.forward(q, k, v, out=torch.empty_like(q), ws=ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.forward(q, k, v, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.forward(q, k, v, out=out, ws=ws)
+    for i in range(4):
+        out.zero_()
+        ws.zero_()
+        junk = torch.randn(4096, device=dev).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {i} differs ({junk.item():.1f})"
