@@ -56,12 +56,16 @@ constexpr int kWideMaxGroups = 128;  // a level is wide when groups x problems i
 
 __device__ __forceinline__ float bf(uint32_t b) { return __uint_as_float(b << 16); }
 
-__device__ __forceinline__ uint32_t to_bf16(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to nearest-even bf16 by one v_cvt_pk_bf16_f32, packed
+// as (lo | hi << 16).
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  const bf16x2 t = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, t);
 }
+
+__device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)(bf16_pair(x, 0.0f) & 0xffffu); }
 
 struct Prob {
   int b, h, side;
@@ -180,7 +184,8 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(Shape s, Workspace ws)
   if (e >= D * D) return;
   const float* part = ws.rb_part + (long long)p * s.rb_chunks * D * D + e;
   float m = 0.0f;
-  for (int c = 0; c < s.rb_chunks; ++c) m += part[(long long)c * D * D];
+#pragma unroll 8
+  for (int c = 0; c < s.rb_chunks; ++c) m += part[(long long)c * D * D];  // loads batched, sums in order
   ws.rb_M[(long long)p * D * D + e] = m;
 }
 
@@ -205,7 +210,19 @@ __global__ __launch_bounds__(256) void embed_kernel(Shape s, const uint16_t* __r
   const uint16_t* x = rows_of(s, pr, q, k, false);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
   const float* M = ws.rb_M + (long long)p * D * D;
-  for (int i = tid; i < D * D; i += 256) Mb[(i / D) * LP + i % D] = (uint16_t)to_bf16(M[i]);
+  {
+    // M rounded to bf16 into LDS: every thread's 16-byte loads in flight at
+    // once (one load at a time took tens of microseconds per workgroup)
+    constexpr int MV = D * D / 4 / 256;
+    float4 mv[MV];
+#pragma unroll
+    for (int u = 0; u < MV; ++u) mv[u] = reinterpret_cast<const float4*>(M)[tid + 256 * u];
+#pragma unroll
+    for (int u = 0; u < MV; ++u) {
+      const int i = 4 * (tid + 256 * u), row = i / D, col = i % D;
+      *reinterpret_cast<uint2*>(Mb + row * LP + col) = make_uint2(bf16_pair(mv[u].x, mv[u].y), bf16_pair(mv[u].z, mv[u].w));
+    }
+  }
   const int nv = s.rb_n;
   uint16_t* U = ws.rb_U + (long long)p * nv * D;
   uint16_t* MU = ws.rb_MU + (long long)p * nv * D;
@@ -279,8 +296,8 @@ __global__ __launch_bounds__(256) void embed_kernel(Shape s, const uint16_t* __r
         uint32_t wu[4], wm[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          wu[e] = to_bf16(xs[d + 2 * e] * inv) | (to_bf16(xs[d + 2 * e + 1] * inv) << 16);
-          wm[e] = to_bf16(ys[d + 2 * e] * inv) | (to_bf16(ys[d + 2 * e + 1] * inv) << 16);
+          wu[e] = bf16_pair(xs[d + 2 * e] * inv, xs[d + 2 * e + 1] * inv);
+          wm[e] = bf16_pair(ys[d + 2 * e] * inv, ys[d + 2 * e + 1] * inv);
           us[d + 2 * e] += bf(wu[e] & 0xffffu);
           us[d + 2 * e + 1] += bf(wu[e] >> 16);
         }
@@ -826,7 +843,8 @@ __global__ __launch_bounds__(256) void wide_pass_kernel(Shape s, int level, int 
   if (tid < D) {
     if (phase == 1) {
       float t = 0.0f;
-      for (int i = 0; i < nc; ++i) t += sums[(long long)i * D + tid];
+#pragma unroll 8
+      for (int i = 0; i < nc; ++i) t += sums[(long long)i * D + tid];  // loads batched, sums in order
       vec[tid] = t / (float)n;
     } else {
       const float xa = bf(U[(long long)oin[piv[0]] * D + tid]);
