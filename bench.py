@@ -175,7 +175,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--graph", action="store_true", help="also time the call replayed from a HIP graph")
-    ap.add_argument("--no-modes", action="store_true", help="skip the reweight, INT8 QK^T, strided fused-QKV and reblock timings")
+    ap.add_argument("--no-modes", action="store_true", help="skip the reweight, INT8 QK^T, exact_kv (with a prefix), strided fused-QKV and reblock timings")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 256 MiB device copy before the steps (scales rocprofv3 byte counters)")
@@ -300,7 +300,10 @@ def main():
     modes = None
     if not args.no_modes:
         modes = {}
-        for name, extra in (("reweight", dict(reweight=True)), ("int8_qk", dict(int8_qk=True))):
+        variants = [("reweight", dict(reweight=True)), ("int8_qk", dict(int8_qk=True))]
+        if w.prefix_len > 0:  # the sink without the dense prefix query rows
+            variants.append(("exact_kv", dict(exact_kv_only=True)))
+        for name, extra in variants:
             mplan = binding.SparseAttnPlan(B, N, H, D, prefix_len=w.prefix_len, **rkw, **extra)
             mws = mplan.workspace(dev)
             for _ in range(2):
