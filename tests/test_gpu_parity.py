@@ -1237,3 +1237,61 @@ def test_graph_capture_replays_match_eager(kw):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {i} differs ({junk.item():.1f})"
+
+
+# ------------------------------------------- seeded random large configurations
+#
+# N from 4000 to 40000 (n_b 63 to 625: long lists, many centroid half tiles,
+# union tables refilled), one or two heads, random routing, prefix and
+# flags on soft clustered inputs; every list against the oracle, and 16
+# sampled query blocks plus the tail and prefix boundary blocks.
+
+def _random_large_config(seed):
+    rng = np.random.default_rng(5000 + seed)
+    H, D = int(rng.integers(1, 3)), int(rng.choice([64, 128]))
+    N = int(rng.integers(4000, 40001))
+    kw = {}
+    if rng.random() < 0.5:
+        kw["tau"] = float(rng.choice([0.0, 0.5, 1.0, 2.0]))
+    else:
+        kw["topk_ratio"] = float(rng.choice([0.05, 0.1, 0.2]))
+    if rng.random() < 0.6:
+        kw["prefix_len"] = int(rng.integers(1, 2049))
+    if rng.random() < 0.15:
+        kw["centroid"] = False
+    elif rng.random() < 0.3:
+        kw["reweight"] = True
+    if rng.random() < 0.15:
+        kw["logmass"] = False
+    if rng.random() < 0.3:
+        kw["int8_qk"] = True
+    if "prefix_len" in kw and rng.random() < 0.3:
+        kw["exact_kv_only"] = True
+    return dict(B=1, N=N, H=H, D=D), kw
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_large_configurations(seed):
+    shape, kw = _random_large_config(seed)
+    B, N, H, D = shape["B"], shape["N"], shape["H"], shape["D"]
+    print(f"  seed {seed}: B={B} N={N} H={H} D={D} {kw}", flush=True)
+    q, k, v = inputs.clustered_soft(B, N, H, D, seed=seed + 300)
+    run = GpuRun(q, k, v, **kw)
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    okw = oracle_kw(kw)
+    _, info = O.forward_blocks(qf, kf, vf, [], **okw)
+    sel = run.selection()
+    frac = check_route(sel, info)
+    nb = O.num_blocks(N)
+    rng = np.random.default_rng(seed)
+    blocks = {(0, int(rng.integers(H)), int(rng.integers(nb))) for _ in range(16)}
+    blocks |= {(0, 0, nb - 1), (0, H - 1, 0)}
+    pb = O.prefix_blocks(kw.get("prefix_len", 0))
+    if 0 < pb < nb:
+        blocks |= {(0, 0, pb - 1), (0, H - 1, pb)}
+    parts, _ = O.forward_blocks(qf, kf, vf, sorted(blocks), info=dict(info, sel=sel), **okw)
+    got = run.out_f64()
+    g = np.concatenate([got[b, a * 64 : a * 64 + r.shape[0], h] for (b, h, a), r in parts.items()])
+    r = np.concatenate(list(parts.values()))
+    print(f"  density {sel.mean():.4f} band {frac:.2e}", flush=True)
+    check_output(g, r, f"seed {seed} ({len(parts)} blocks)")
