@@ -180,7 +180,9 @@ typedef struct sparse_attn_plan sparse_attn_plan; /* opaque, host memory */
  * With SA_FLAG_REBLOCK only (problem p = side * B * H + b * H + h, side 0 =
  * query rows; side 1 = key rows exists with SA_FLAG_REBLOCK_KV_OWN only, so
  * P = B H problems, or 2 B H with it; n_v = N - 64 * prefix_blocks rows move):
- *   rb_gram           fp32 partial second moments (scratch).
+ *   rb_gram           fp32 scratch: partial second moments, then (once M
+ *                     is reduced) the partial sums and minima of the split
+ *                     levels run over 1024-row chunks.
  *   rb_metric         fp32 [P, D, D]: M = Y^T Y of the other side.
  *   rb_units          bf16 [P, n_v, D]: the unit rows u of the moving rows.
  *   rb_munits         bf16 [P, n_v, D]: M u of the same rows (the split
