@@ -1295,3 +1295,34 @@ def test_random_large_configurations(seed):
     r = np.concatenate(list(parts.values()))
     print(f"  density {sel.mean():.4f} band {frac:.2e}", flush=True)
     check_output(g, r, f"seed {seed} ({len(parts)} blocks)")
+
+
+def test_reblock_max_blocks():
+    """Spark-Reblock at n_b = 2048 (N = 131072, the largest supported length),
+    one head: an 11-level tree whose first seven levels run over 1024-row
+    chunks.  Every split against the oracle's values from the raw inputs,
+    the lists against the oracle on the GPU's order, and sampled output
+    blocks."""
+    B, N, H, D = 1, 131072, 1, 128
+    q, k, v = inputs.clustered_soft(B, N, H, D, seed=13)
+    run = GpuRun(q, k, v, reblock=True, tau=1.0)
+    M, U, MU, pq, pk = run.plan.reblock_views(run.ws)
+    pq, pk = pq.cpu().numpy(), pk.cpu().numpy()
+    assert (pk == pq).all() and sorted(pq[0, 0].tolist()) == list(range(N))
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    u_ref, M_ref = O.mahalanobis_units(qf[0, :, 0], kf[0, :, 0])
+    Mg = M.cpu().numpy().astype(np.float64)[0, 0, 0]
+    np.testing.assert_allclose(Mg, M_ref, rtol=0, atol=1e-4 * np.abs(M_ref).max())
+    ns, nl_ = check_reblock_tree(pq[0, 0], u_ref, M_ref)
+    print(f"  n_b 2048 reblock: {ns} splits against the oracle's values ({nl_} rows within tol of a cut)", flush=True)
+    assert nl_ <= 0.02 * N
+    qp, kp, vp = _permute(qf, pq), _permute(kf, pk), _permute(vf, pk)
+    _, info = O.forward_blocks(qp, kp, vp, [], tau=1.0)
+    sel = run.selection()
+    check_route(sel, info)
+    blocks = [(0, 0, a) for a in (0, 1, 777, 1500, 2047)]
+    parts, _ = O.forward_blocks(qp, kp, vp, blocks, info=dict(info, sel=sel), tau=1.0)
+    got = run.out_f64()
+    for (b, h, a), ref in parts.items():
+        rows = pq[b, h, a * 64 : a * 64 + ref.shape[0]]
+        check_output(got[b, rows, h], ref, f"reblock block {a}")
