@@ -362,3 +362,28 @@ def test_launch_grid_limits(lib):
     assert "REBLOCK" in lib.sparse_attn_last_error().decode()
     assert _create(lib, _params(B=1, N=64, H=40000, flags=3 | 32 | 64)) == SA_EUNSUPPORTED_SHAPE
     assert "2*B*H" in lib.sparse_attn_last_error().decode()
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built library every entry point raises: there is no
+    other implementation to fall back to (checked in a fresh process)."""
+    code = (
+        "import torch\n"
+        "from block_sparse_video_fp32_amd import binding\n"
+        "for f in (binding.load_library,\n"
+        "          lambda: binding.SparseAttnPlan(1, 128, 1, 64, tau=1.0),\n"
+        "          lambda: binding.sparse_attn(*(torch.zeros(1, 128, 1, 64, dtype=torch.bfloat16) for _ in range(3)))):\n"
+        "    try:\n"
+        "        f()\n"
+        "    except ImportError as e:\n"
+        "        assert 'not found' in str(e), e\n"
+        "    else:\n"
+        "        raise SystemExit('no error')\n"
+        "print('ok')\n"
+    )
+    import subprocess
+    import sys
+
+    env = dict(os.environ, SPARSE_ATTN_LIB=str(tmp_path / "absent.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
