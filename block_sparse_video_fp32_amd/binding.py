@@ -131,8 +131,7 @@ def load_library() -> ctypes.CDLL:
         if not os.path.exists(path):
             raise ImportError(
                 f"{path} not found: build the HIP library first "
-                "(python -c 'import __graft_entry__ as g; g.build()' or "
-                "python -m block_sparse_video_fp32_amd.build)"
+                "(python -m block_sparse_video_fp32_amd.build)"
             )
         lib = ctypes.CDLL(path)
         vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
