@@ -79,5 +79,9 @@ hipError_t launch_reblock_partition(const Shape& s, const void* q, const void* k
                                     hipStream_t stream);
 hipError_t launch_attend(const Shape& s, const void* q, void* out, const Workspace& ws,
                          hipStream_t stream);
+// tau = -inf with bf16 QK^T (dense_attend_kernels.hip): four query blocks per
+// workgroup, the same result as launch_attend bit for bit.
+hipError_t launch_dense_attend(const Shape& s, const void* q, void* out, const Workspace& ws,
+                               hipStream_t stream);
 
 }  // namespace sa

@@ -412,6 +412,14 @@ int sparse_attn_select(const sparse_attn_plan* plan, void* ws, size_t ws_bytes, 
   return ok();
 }
 
+// The attend step: the dense path (tau = -inf, bf16 QK^T, rows in place)
+// has a kernel of its own; everything else runs the routed kernel.
+static hipError_t attend(const sa::Shape& s, const void* q, void* out, const sa::Workspace& w,
+                         hipStream_t st) {
+  if (s.dense && !s.int8 && !s.permuted) return sa::launch_dense_attend(s, q, out, w, st);
+  return sa::launch_attend(s, q, out, w, st);
+}
+
 int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, void* out, void* ws, size_t ws_bytes,
                        void* stream) {
   if (!plan) return fail(SA_EINVAL, "plan is NULL");
@@ -420,7 +428,7 @@ int sparse_attn_attend(const sparse_attn_plan* plan, const void* q, void* out, v
   if ((rc = check_tensors(q, q, q, out, true))) return rc;
   if ((rc = check_ws(plan, ws, ws_bytes))) return rc;
   if ((rc = check_device())) return rc;
-  if ((rc = launched(sa::launch_attend(plan->shape, q, out, carve(plan, ws), (hipStream_t)stream), "attend")))
+  if ((rc = launched(attend(plan->shape, q, out, carve(plan, ws), (hipStream_t)stream), "attend")))
     return rc;
   return ok();
 }
@@ -451,7 +459,7 @@ int sparse_attn_forward(const sparse_attn_plan* plan, const void* q, const void*
   if (!s.dense) {
     if ((rc = launched(sa::launch_select(s, w, st), "select"))) return rc;
   }
-  if ((rc = launched(sa::launch_attend(s, q, out, w, st), "attend"))) return rc;
+  if ((rc = launched(attend(s, q, out, w, st), "attend"))) return rc;
   return ok();
 }
 

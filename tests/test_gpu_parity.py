@@ -359,6 +359,26 @@ def test_logit_spike_recompute(D, tau, int8_qk):
     full_parity(q, k, v, tau=tau, int8_qk=int8_qk)
 
 
+# The dense path (tau = -inf) has a kernel of its own at D = 64 and 128 (four
+# query blocks per workgroup, 64 rows per wave).  Each of its rows does the
+# same arithmetic in the same order as the routed kernel does when every
+# key block is selected (top-K ratio 1: ascending exact tiles, no centroid
+# tiles), so the two outputs agree bit for bit; the routed kernel is checked
+# against the oracle throughout this file.
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 128), (1, 65, 2, 128), (2, 777, 3, 128), (1, 4133, 2, 128),
+                                   (1, 256, 2, 64), (2, 1100, 2, 64), (1, 6000, 1, 128)],
+                         ids=lambda t: "B{}_N{}_H{}_D{}".format(*t))
+def test_dense_kernel_matches_all_selected(shape):
+    B, N, H, D = shape
+    q, k, v = inputs.clustered_soft(B, N, H, D, seed=N) if N >= 256 else inputs.iid(B, N, H, D, seed=N)
+    dense = GpuRun(q, k, v, tau=-math.inf)
+    full = GpuRun(q, k, v, topk_ratio=1.0)
+    assert full.selection().all()
+    a, b = dense.out.view(torch.int16), full.out.view(torch.int16)
+    assert torch.equal(a, b), f"{int((a != b).sum())} of {a.numel()} elements differ"
+
+
 def test_tiny_matches_oracle_lists_exactly():
     w = inputs.make_workload("tiny")
     run = GpuRun(w.q, w.k, w.v, tau=1.0)
