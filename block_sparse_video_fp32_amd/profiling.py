@@ -110,12 +110,15 @@ def counter_per_dispatch(dirname: str, counter: str, kernel_substr: str):
     return out, names
 
 
-def kernel_source_hash() -> str:
-    """Hash of the attend kernel's source file without comment lines, end of
-    line comments and blank lines, so that edits of comments alone do not
-    mark the recorded counters as stale."""
+def kernel_source_hash(kernel: str = "attend_kernel") -> str:
+    """Hash of the source file that holds `kernel` (the dense path's kernel
+    has a file of its own; every other kernel of the path is in
+    sparse_attn_kernels.hip) without comment lines, end of line comments and
+    blank lines, so that edits of comments alone do not mark the recorded
+    counters as stale."""
+    name = "dense_attend_kernels.hip" if kernel.startswith("dense_attend") else "sparse_attn_kernels.hip"
     lines = []
-    with open(os.path.join(HERE, "csrc", "sparse_attn_kernels.hip"), encoding="utf-8") as f:
+    with open(os.path.join(HERE, "csrc", name), encoding="utf-8") as f:
         for line in f:
             code = line.split("//", 1)[0].rstrip()
             if code.strip():
@@ -124,7 +127,7 @@ def kernel_source_hash() -> str:
 
 
 def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int):
-    res = {"kernel": kernel, "copy_bytes": copy_bytes, "kernel_source_sha256_16": kernel_source_hash()}
+    res = {"kernel": kernel, "copy_bytes": copy_bytes, "kernel_source_sha256_16": kernel_source_hash(kernel)}
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals, _ = counter_per_dispatch(d, counter, kernel)
@@ -196,7 +199,7 @@ def mfma(pmc_dir: str, bench_line: dict, kernel: str):
     expected = bench_line.get("attend_mfma_per_launch")
     res = {
         "kernel": kernel,
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash(kernel),
         "dispatches": ndisp,
         "counters_per_dispatch": per,
         "duration_us": dur_ns / 1e3,
@@ -243,7 +246,7 @@ def counters(pmc_dir: str, kernel: str):
         per[c] = sum(vals.values()) / len(vals)
         ndisp = len(vals)
     dur = dispatch_durations(pmc_dir, kernel)
-    res = {"kernel": kernel, "kernel_source_sha256_16": kernel_source_hash(), "dispatches": ndisp,
+    res = {"kernel": kernel, "kernel_source_sha256_16": kernel_source_hash(kernel), "dispatches": ndisp,
            "counters_per_dispatch": per, "duration_us": sum(dur.values()) / len(dur) / 1e3}
     if "GRBM_GUI_ACTIVE" in per:
         gx = per["GRBM_GUI_ACTIVE"] / N_XCD
