@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Q[64 a + 32 t + l % 32][16 k + 8 (l/32) .. +8]; half 1's go to this
   // wave's 8 KB of LDS after the ring.
   bf16x8 qa[NK];
-  const uint8_t* const qlds = ring + S * STAGE + w * NK * 1024;
+  uint8_t* const qlds = ring + S * STAGE + w * NK * 1024;
   {
     const int r0 = a * kBlock + l32, r1 = r0 + 32;
     const uint16_t* qp = q + (long long)b * s.isb + (long long)h * s.ish + 8 * hh;
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (exists && r0 < N) v0 = *reinterpret_cast<const uint4*>(qp + (long long)r0 * s.ist + 16 * k);
       if (exists && r1 < N) v1 = *reinterpret_cast<const uint4*>(qp + (long long)r1 * s.ist + 16 * k);
       qa[k] = __builtin_bit_cast(bf16x8, v0);
-      *reinterpret_cast<uint4*>(const_cast<uint8_t*>(qlds) + k * 1024 + lane * 16) = v1;
+      *reinterpret_cast<uint4*>(qlds + k * 1024 + lane * 16) = v1;
     }
   }
 

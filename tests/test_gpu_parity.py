@@ -1229,8 +1229,8 @@ def test_random_configurations(seed):
 # must equal the eager call bit for bit.
 
 @pytest.mark.parametrize("kw", [dict(tau=1.0, prefix_len=100), dict(topk_ratio=0.2, reweight=True, int8_qk=True),
-                                dict(tau=1.0, prefix_len=70, reblock=True)],
-                         ids=["tau_prefix", "topk_reweight_int8", "reblock"])
+                                dict(tau=1.0, prefix_len=70, reblock=True), dict(tau=-math.inf)],
+                         ids=["tau_prefix", "topk_reweight_int8", "reblock", "dense"])
 def test_graph_capture_replays_match_eager(kw):
     dev = _dev()
     B, N, H, D = 1, 3000, 4, 128
