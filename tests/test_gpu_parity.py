@@ -1221,6 +1221,33 @@ def test_random_configurations(seed):
         full_parity(q, k, v, **kw)
 
 
+# Seeded random shapes through the dense path (tau = -inf: the dense kernel
+# at D = 64 and 128, or the routed kernel with INT8 QK^T), every output row
+# against the oracle's softmax over all keys.
+
+def _random_dense_config(seed):
+    rng = np.random.default_rng(3000 + seed)
+    B, H, D = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.choice([64, 128]))
+    N = int(rng.integers(1, 65)) if rng.random() < 0.25 else int(rng.integers(65, 3001))
+    kw = dict(tau=-math.inf)
+    if rng.random() < 0.25:
+        kw["sm_scale"] = float(rng.uniform(0.05, 0.2))
+    if seed % 4 == 3:  # a quarter of the cases through the INT8 QK^T kernel
+        kw["int8_qk"] = True
+    soft = N >= 256 and rng.random() < 0.5
+    return dict(B=B, N=N, H=H, D=D, soft=soft), kw
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_dense_configurations(seed):
+    shape, kw = _random_dense_config(seed)
+    B, N, H, D = shape["B"], shape["N"], shape["H"], shape["D"]
+    print(f"  seed {seed}: B={B} N={N} H={H} D={D} soft={shape['soft']} {kw}", flush=True)
+    gen = inputs.clustered_soft if shape["soft"] else inputs.iid
+    q, k, v = gen(B, N, H, D, seed=seed + 90)
+    full_parity(q, k, v, **kw)
+
+
 # ------------------------------------------------------------ graph capture
 #
 # The library launches only kernels on the caller's stream (no memset, no
